@@ -1,0 +1,266 @@
+"""fp64 CPU oracle for Elastic Attention's prefill path (router + hybrid-head GQA attention).
+
+TEST INFRASTRUCTURE ONLY.  This module is the slow, plain definition that the GPU
+library is checked against.  Only the test suite, the package smoke check and the
+CPU-baseline leg of the benchmark may import or call it; the product path never
+does, and it shares no code with the HIP library.
+
+Source: "Elastic Attention: Test-time Adaptive Sparsity Ratios for Efficient
+Transformers" (arXiv 2601.17367), as summarised on paperlayer.ai
+(abs/2601.17367v2).  Sections cited below are that summary's headings.
+
+What is computed (readings of points the summary leaves open are marked READING):
+
+* Router (section 1 "Introduction": head-wise routing from the layer's input hidden
+  states; section 3 "Attention Router": pooled states -> task/router MLP -> head-wise
+  logits -> binary full/sparse choice per KV head).
+  READING: the pooled state is the arithmetic mean of the layer-input hidden
+  states over all tokens of a sequence (boundary pooling of the first/last tokens,
+  appendix H.4 "Router Input Length", is selectable with ``pool_head/pool_tail``);
+  the MLP is z = W1 h, a = ReLU(z), l = W2 a with no biases; a KV head is FULL
+  iff l > threshold (ties go to sparse).  Sums are exact (``math.fsum``).
+* Allowed key sets (section 2 "Hybrid Head Mechanism"; section 4 and appendix B.2
+  for streaming sparse attention; appendix D.1 "Sparse Inference" for block
+  sparsity).  Positions are local to a sequence; every set contains j = i.
+    full:       {j <= i}
+    streaming:  {j <= i : j < sink  or  i - j < window}            (READING: window includes i)
+    block:      {j <= i : j//B in K(i//B)},  K(qb) = {kb < sink_blocks}
+                  U {qb-local_blocks .. qb}  U {kb : stride > 0 and kb % stride == 0}
+  Query head h reads KV head h // G (GQA, repeat_kv convention) and takes that KV
+  head's mode (section 3 "Attention Router": one decision per key-value head).
+* Attention: exact two-pass softmax over the allowed set, s_j = scale <q_i, k_j>,
+  scale = D^-1/2 unless given; o_i = sum_j softmax(s)_j v_j; lse_i = m + log sum exp(s - m).
+  Head outputs are concatenated (o is [T, Hq, D]).
+* Counters: entries (allowed (query, key) pairs over all query heads), effective
+  FLOPs = 4*D*entries, model sparsity ratio (fraction of sparse heads) and effective
+  sparsity (section 2 "Sparsity Ratio Computation").
+"""
+from __future__ import annotations
+
+import math
+from contextlib import nullcontext
+from concurrent.futures import ThreadPoolExecutor
+from typing import Optional, Sequence
+
+import numpy as np
+
+try:  # keep BLAS single-threaded inside the oracle's own thread pool
+    from threadpoolctl import threadpool_limits
+except Exception:  # pragma: no cover
+    threadpool_limits = None
+
+
+# ----------------------------------------------------------------------------- inputs
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """Exact float64 values of bfloat16 bit patterns (uint16)."""
+    b = np.ascontiguousarray(bits).view(np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def as_f64(x: np.ndarray) -> np.ndarray:
+    """uint16 arrays are bf16 bit patterns; float arrays are taken at face value."""
+    if x.dtype == np.uint16:
+        return decode_bf16(x)
+    return np.asarray(x, dtype=np.float64)
+
+
+def _seq_bounds(cu_seqlens: Optional[Sequence[int]], total: int) -> np.ndarray:
+    if cu_seqlens is None:
+        return np.array([0, total], dtype=np.int64)
+    return np.asarray(cu_seqlens, dtype=np.int64)
+
+
+# ----------------------------------------------------------------------------- router
+def pooled_rows(n: int, pool_head: int = 0, pool_tail: int = 0) -> np.ndarray:
+    """Local row indices the router pools for a sequence of length n.
+
+    0,0 -> every row.  Otherwise the first ``pool_head`` and the last ``pool_tail``
+    rows (appendix H.4, boundary pooling); when they overlap, each row counts once."""
+    if pool_head == 0 and pool_tail == 0:
+        return np.arange(n)
+    rows = set(range(min(n, pool_head))) | set(range(max(0, n - pool_tail), n))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def mean_exact(x: np.ndarray) -> np.ndarray:
+    """Column means of a 2-D array with correctly rounded column sums (math.fsum)."""
+    n, d = x.shape
+    out = np.empty(d, dtype=np.float64)
+    step = 256
+    for c0 in range(0, d, step):
+        cols = np.ascontiguousarray(x[:, c0:c0 + step].T).tolist()
+        for c, col in enumerate(cols):
+            out[c0 + c] = math.fsum(col) / n
+    return out
+
+
+def route(hidden: np.ndarray, cu_seqlens, w1: np.ndarray, w2: np.ndarray,
+          threshold: float = 0.0, pool_head: int = 0, pool_tail: int = 0) -> dict:
+    """Attention Router forward for every sequence of a packed batch.
+
+    hidden [T, d] (bf16 bits or float), w1 [d_router, d], w2 [Hkv, d_router].
+    Returns pooled [B, d], hidden-layer z [B, d_router], logits [B, Hkv] (fp64) and
+    mask [B, Hkv] int32 with 1 = full attention, 0 = sparse attention."""
+    x = as_f64(hidden)
+    W1 = np.asarray(w1, dtype=np.float64)
+    W2 = np.asarray(w2, dtype=np.float64)
+    cu = _seq_bounds(cu_seqlens, x.shape[0])
+    B = len(cu) - 1
+    pooled = np.zeros((B, x.shape[1]))
+    z = np.zeros((B, W1.shape[0]))
+    logits = np.zeros((B, W2.shape[0]))
+    for b in range(B):
+        n = int(cu[b + 1] - cu[b])
+        rows = pooled_rows(n, pool_head, pool_tail) + cu[b]
+        pooled[b] = mean_exact(x[rows])
+        z[b] = W1 @ pooled[b]
+        a = np.maximum(z[b], 0.0)
+        logits[b] = W2 @ a
+    mask = (logits > threshold).astype(np.int32)
+    return {"pooled": pooled, "z": z, "logits": logits, "mask": mask}
+
+
+# ----------------------------------------------------------------------------- masks
+def allowed(i, j, full: bool, sparse: Optional[dict]) -> np.ndarray:
+    """Boolean (broadcast over i, j): may query position i attend key position j?"""
+    i = np.asarray(i, dtype=np.int64)
+    j = np.asarray(j, dtype=np.int64)
+    causal = j <= i
+    if full:
+        return causal
+    kind = sparse["kind"]
+    if kind == "streaming":
+        return causal & ((j < sparse["sink"]) | (i - j < sparse["window"]))
+    if kind == "block":
+        B = sparse["block"]
+        qb, kb = i // B, j // B
+        keep = (kb < sparse["sink_blocks"]) | (qb - kb <= sparse["local_blocks"])
+        stride = sparse["stride_blocks"]
+        if stride > 0:
+            keep = keep | (kb % stride == 0)
+        return causal & keep
+    raise ValueError(f"unknown sparse kind {kind!r}")
+
+
+def row_key_counts(n: int, full: bool, sparse: Optional[dict], rows=None,
+                   block_rows: int = 256) -> np.ndarray:
+    """|A(i)| for the given local rows (default all), by enumerating the mask."""
+    rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.empty(len(rows), dtype=np.int64)
+    for r0 in range(0, len(rows), block_rows):
+        ii = rows[r0:r0 + block_rows]
+        jj = np.arange(int(ii.max()) + 1)
+        out[r0:r0 + block_rows] = allowed(ii[:, None], jj[None, :], full, sparse).sum(axis=1)
+    return out
+
+
+def head_modes(head_mask, batch: int, n_kv_heads: int) -> np.ndarray:
+    """[B, Hkv] bool, True = full.  ``None`` means every head is full."""
+    if head_mask is None:
+        return np.ones((batch, n_kv_heads), dtype=bool)
+    return np.asarray(head_mask).reshape(batch, n_kv_heads) != 0
+
+
+def entries(seqlens, head_mask, sparse, n_q_heads: int, n_kv_heads: int) -> int:
+    """Allowed (query, key) pairs summed over all query heads and sequences."""
+    G = n_q_heads // n_kv_heads
+    modes = head_modes(head_mask, len(seqlens), n_kv_heads)
+    cache = {}
+    total = 0
+    for b, n in enumerate(seqlens):
+        for g in range(n_kv_heads):
+            key = (int(n), bool(modes[b, g]))
+            if key not in cache:
+                cache[key] = int(row_key_counts(int(n), key[1], sparse).sum())
+            total += G * cache[key]
+    return total
+
+
+def effective_flops(n_entries: int, head_dim: int) -> int:
+    """Q.K^T and P.V each cost 2*D FLOPs per allowed score entry."""
+    return 4 * head_dim * n_entries
+
+
+def model_sparsity_ratio(head_mask, seqlens=None, token_weighted: bool = False) -> float:
+    """Fraction of sparse heads (optionally weighting each sequence by its length)."""
+    m = np.asarray(head_mask) != 0
+    if not token_weighted:
+        return float((~m).sum() / m.size)
+    w = np.asarray(seqlens, dtype=np.float64)[:, None]
+    return float(((~m) * w).sum() / (w.sum() * m.shape[1]))
+
+
+def effective_sparsity(seqlens, head_mask, sparse, n_q_heads, n_kv_heads) -> float:
+    """1 - (allowed entries) / (entries of all-full causal attention)."""
+    dense = sum(n_q_heads * n * (n + 1) // 2 for n in seqlens)
+    return 1.0 - entries(seqlens, head_mask, sparse, n_q_heads, n_kv_heads) / dense
+
+
+# ----------------------------------------------------------------------------- attention
+def _attend_block(Q, K, V, ii, full, sparse, scale):
+    """Rows ``ii`` (local positions) of one query head: exact two-pass softmax."""
+    jj = np.arange(int(ii.max()) + 1)
+    A = allowed(ii[:, None], jj[None, :], full, sparse)
+    cols = np.nonzero(A.any(axis=0))[0]
+    A = A[:, cols]
+    s = scale * (Q[ii] @ K[cols].T)
+    s = np.where(A, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)                      # exp(-inf) = 0 for disallowed keys
+    denom = p.sum(axis=1, keepdims=True)
+    o = (p @ V[cols]) / denom
+    lse = m[:, 0] + np.log(denom[:, 0])
+    return o, lse
+
+
+def attention(q, k, v, cu_seqlens, head_mask, sparse, scale: Optional[float] = None,
+              rows=None, heads=None, block_rows: int = 64, workers: int = 1):
+    """Hybrid-head GQA prefill attention.
+
+    q [T, Hq, D], k/v [T, Hkv, D] (bf16 bit patterns or floats); head_mask [B, Hkv]
+    (1 = full; None = all full); sparse = pattern dict for the sparse heads.
+    ``rows``: sorted global token indices to evaluate (default all); ``heads``:
+    query heads to evaluate (default all).  Returns o [len(rows), len(heads), D]
+    and lse [len(heads), len(rows)] in float64."""
+    Qa, Ka, Va = as_f64(q), as_f64(k), as_f64(v)
+    T, Hq, D = Qa.shape
+    Hkv = Ka.shape[1]
+    G = Hq // Hkv
+    scale = D ** -0.5 if scale is None or scale <= 0 else float(scale)
+    cu = _seq_bounds(cu_seqlens, T)
+    B = len(cu) - 1
+    modes = head_modes(head_mask, B, Hkv)
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    heads = list(range(Hq)) if heads is None else list(heads)
+    seq_of = np.searchsorted(cu, rows, side="right") - 1
+    o = np.zeros((len(rows), len(heads), Va.shape[2]))
+    lse = np.zeros((len(heads), len(rows)))
+
+    tasks = []
+    for b in range(B):
+        sel = np.nonzero(seq_of == b)[0]
+        if len(sel) == 0:
+            continue
+        for hi, h in enumerate(heads):
+            for r0 in range(0, len(sel), block_rows):
+                tasks.append((b, hi, h, sel[r0:r0 + block_rows]))
+
+    def run(task):
+        b, hi, h, sel = task
+        lo, hi_tok = int(cu[b]), int(cu[b + 1])
+        g = h // G
+        Q = Qa[lo:hi_tok, h, :]
+        K = Ka[lo:hi_tok, g, :]
+        V = Va[lo:hi_tok, g, :]
+        ob, lb = _attend_block(Q, K, V, rows[sel] - lo, bool(modes[b, g]), sparse, scale)
+        o[sel, hi, :] = ob
+        lse[hi, sel] = lb
+
+    if workers <= 1:
+        for t in tasks:
+            run(t)
+    else:
+        limit = threadpool_limits(limits=1) if threadpool_limits is not None else nullcontext()
+        with limit, ThreadPoolExecutor(workers) as ex:
+            list(ex.map(run, tasks))
+    return o, lse
