@@ -1,0 +1,230 @@
+"""Benchmark of the Elastic Attention prefill hot path on one MI355X.
+
+One step = the whole path for one layer on one batch of synthetic input already resident
+in HBM: router (pool, MLP, threshold) -> scheduler -> hybrid-head GQA attention.
+Prints ONE JSON line (rank 0) with the effective attention TFLOP/s (FLOPs counted only over
+allowed score entries, 4 * head_dim per entry) over the step time, ms per layer, the
+attention kernel's roofline fraction against the bf16 dense MFMA peak, and the fp64 CPU
+oracle timed on a bounded row sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+DEFAULT_WORKLOAD = "llama8b-32k-block-router"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
+    p.add_argument("--no-supplements", action="store_true")
+    p.add_argument("--scaling", action="store_true", help="streaming-window and length scaling sweep")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (the hot path runs on a single device); "
+              f"--gpus {args.gpus} / WORLD_SIZE {world} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import hybrid_sparse_full_elastic_amd as ext
+    from synth import inputs as syn
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    w = syn.WORKLOADS[args.workload]
+    assert w.dtype == "bf16", "the timed workload is a bf16 layer"
+
+    def dev_t(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    t_gen = time.time()
+    data = syn.make_qkv(w)
+    q, k, v = dev_t(data["q"]), dev_t(data["k"]), dev_t(data["v"])
+    has_router = w.router is not None
+    if has_router:
+        rin = syn.make_router_inputs(w)
+        hidden, w1, w2 = dev_t(rin["hidden"]), dev_t(rin["w1"]), dev_t(rin["w2"])
+        threshold = rin["threshold"]
+        del rin
+    cu = torch.tensor(w.cu_seqlens(), dtype=torch.int32, device=dev)
+    T, hq, D = q.shape
+    hkv = k.shape[1]
+    B = w.batch
+    o = torch.empty_like(q)
+    logits = torch.empty((B, hkv), dtype=torch.float32, device=dev)
+    mask = torch.empty((B, hkv), dtype=torch.int32, device=dev)
+    if not has_router:
+        fm = syn.forced_mask(w)
+        mask.copy_(torch.from_numpy(fm))
+    ws_attn = torch.empty(ext.attn_workspace_size(0, B, T, hq, hkv, D), dtype=torch.uint8, device=dev)
+    ws_route = torch.empty(max(1, ext.route_workspace_size(B, T, w.router["d_model"]) if has_router else 1),
+                           dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    gen_s = time.time() - t_gen
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if has_router:
+            if ev is not None:
+                ev[0].record(stream)
+            ext.route(hidden, w1, w2, cu_seqlens=cu, threshold=threshold, logits=logits, mask=mask,
+                      workspace=ws_route)
+        if ev is not None:
+            ev[1].record(stream)
+        ext.attn_prefill(q, k, v, cu_seqlens=cu, max_seqlen=w.max_seqlen, head_mask=mask,
+                         sparse=w.sparse, out=o, workspace=ws_attn)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    route_ms = [e[0].elapsed_time(e[1]) for e in evs] if has_router else [0.0]
+
+    # work actually done, from the mask the router produced (host closed forms)
+    mask_h = mask.cpu().numpy()
+    entries = ext.attn_entries(list(w.seqlens), mask_h, hq, hkv, w.sparse)
+    flops = 4 * D * entries
+    dense = hq * sum(n * (n + 1) // 2 for n in w.seqlens)
+    attn_avg = float(np.mean(attn_ms))
+    attn_tflops = flops / (attn_avg * 1e-3) / 1e12
+    value = flops / (ms_step * 1e-3) / 1e12
+    router_bytes = T * w.router["d_model"] * 2 if has_router else 0
+    route_avg = float(np.mean(route_ms))
+
+    rec = {
+        "metric": "effective attention TFLOP/s + ms/layer, hybrid-head GQA prefill at 32K",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {
+            "workload": w.name, "seq_lens": list(w.seqlens), "n_q_heads": hq, "n_kv_heads": hkv,
+            "head_dim": D, "sparse": w.sparse,
+            "router": {k2: v2 for k2, v2 in (w.router or {}).items()} if has_router else None,
+            "head_mask": mask_h.tolist(),
+            "omega_msr": float((mask_h == 0).mean()),
+            "omega_esr": 1.0 - entries / dense,
+            "effective_flops": flops,
+        },
+        "breakdown": {
+            "router_us": round(route_avg * 1e3, 2),
+            "router_gbs": round(router_bytes / (route_avg * 1e-3) / 1e9, 1) if has_router and route_avg > 0 else None,
+            "attn_ms": round(attn_avg, 4), "attn_ms_p10": round(float(np.percentile(attn_ms, 10)), 4),
+            "attn_ms_p90": round(float(np.percentile(attn_ms, 90)), 4),
+            "attn_tflops": round(attn_tflops, 2),
+            "note": "attn_ms brackets elastic_attn_prefill = scheduler (one small kernel) + attention kernel",
+        },
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "input_gen_s": round(gen_s, 2),
+    }
+
+    if not args.no_supplements:
+        rec["supplements"] = supplements(ext, torch, w, q, k, v, o, cu, ws_attn, stream, args)
+
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, data, mask_h, args.cpu_seconds)
+
+    print(json.dumps(rec), flush=True)
+
+
+def _time_attn(ext, torch, stream, fn, reps=10, warm=3):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def supplements(ext, torch, w, q, k, v, o, cu, ws, stream, args):
+    """Full-heads-only attention on the same tensors (the 50%-of-peak target shape)."""
+    T, hq, D = q.shape
+    hkv = k.shape[1]
+    ms = _time_attn(ext, torch, stream, lambda: ext.attn_prefill(
+        q, k, v, cu_seqlens=cu, max_seqlen=w.max_seqlen, head_mask=None, sparse=None, out=o, workspace=ws))
+    flops = 4 * D * ext.attn_entries(list(w.seqlens), None, hq, hkv, None)
+    out = {"full_heads_only": {"attn_ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 2),
+                               "frac_bf16_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}}
+    all_sparse = torch.zeros((w.batch, hkv), dtype=torch.int32, device=q.device)
+    ms_s = _time_attn(ext, torch, stream, lambda: ext.attn_prefill(
+        q, k, v, cu_seqlens=cu, max_seqlen=w.max_seqlen, head_mask=all_sparse, sparse=w.sparse, out=o, workspace=ws))
+    flops_s = 4 * D * ext.attn_entries(list(w.seqlens), all_sparse.cpu().numpy(), hq, hkv, w.sparse)
+    out["sparse_heads_only"] = {"attn_ms": round(ms_s, 4), "tflops": round(flops_s / ms_s / 1e9, 2)}
+    return out
+
+
+def cpu_baseline(w, data, mask_h, target_s):
+    """The fp64 oracle on the host cores, on a bounded seeded row sample of the workload."""
+    import oracle
+    from synth import inputs as syn
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))
+    D = w.head_dim
+    rows_per = 8
+    elapsed, flops, nrows = 0.0, 0, 0
+    seed = 0
+    while elapsed < target_s and seed < 64:
+        rows = np.concatenate([syn.spread_rows(int(n), rows_per, seed * 131 + b) + int(w.cu_seqlens()[b])
+                               for b, n in enumerate(w.seqlens)])
+        t = time.time()
+        oracle.attention(data["q"], data["k"], data["v"], w.cu_seqlens(), mask_h, w.sparse,
+                         rows=rows, workers=cores)
+        elapsed += time.time() - t
+        cu = w.cu_seqlens()
+        seq_of = np.searchsorted(cu, rows, side="right") - 1
+        for b in range(w.batch):
+            loc = rows[seq_of == b] - cu[b]
+            for g in range(w.n_kv_heads):
+                cnt = oracle.row_key_counts(int(w.seqlens[b]), bool(mask_h[b, g]), w.sparse, rows=loc)
+                flops += 4 * D * w.group * int(cnt.sum())
+        nrows += len(rows)
+        seed += 1
+    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{nrows} seeded rows x all {w.n_q_heads} query heads of {w.name} "
+                      f"({elapsed:.1f} s, fp64 numpy, {cores} threads)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,206 @@
+"""ctypes binding of libelastic (see include/elastic.h for the contract of each call)."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libelastic.so")
+ABI_VERSION = 1
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
+BF16, FP32 = 0, 1
+STREAMING, BLOCK = 0, 1
+
+
+class ElasticError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = f"{where}: {lib.elastic_status_string(status).decode()}"
+        if status == EHIP:
+            msg += f" ({lib.elastic_last_error().decode()})"
+        super().__init__(msg)
+
+
+class SparseCfg(C.Structure):
+    _fields_ = [("kind", C.c_int32), ("sink_tokens", C.c_int32), ("window_tokens", C.c_int32),
+                ("block_size", C.c_int32), ("sink_blocks", C.c_int32),
+                ("local_blocks", C.c_int32), ("stride_blocks", C.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m hybrid_sparse_full_elastic_amd.build`")
+    L = C.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
+    L.elastic_abi_version.restype = C.c_int
+    L.elastic_abi_version.argtypes = []
+    L.elastic_status_string.restype = C.c_char_p
+    L.elastic_status_string.argtypes = [C.c_int]
+    L.elastic_last_error.restype = C.c_char_p
+    L.elastic_last_error.argtypes = []
+    L.elastic_route_workspace_size.restype = sz
+    L.elastic_route_workspace_size.argtypes = [i32, i64, i32]
+    L.elastic_route.restype = C.c_int
+    L.elastic_route.argtypes = [vp, i32, vp, i32, i64, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp,
+                                vp, sz, vp]
+    L.elastic_attn_workspace_size.restype = sz
+    L.elastic_attn_workspace_size.argtypes = [i32, i32, i64, i32, i32, i32]
+    L.elastic_attn_prefill.restype = C.c_int
+    L.elastic_attn_prefill.argtypes = [vp, vp, vp, vp, i32, vp, i32, i64, i32, i32, i32, i32, f32,
+                                       vp, C.POINTER(SparseCfg), vp, vp, sz, vp]
+    L.elastic_attn_entries.restype = C.c_int
+    L.elastic_attn_entries.argtypes = [C.POINTER(i32), i32, C.POINTER(i32), i32, i32,
+                                       C.POINTER(SparseCfg), C.POINTER(i64)]
+    if L.elastic_abi_version() != ABI_VERSION:
+        raise ImportError(f"libelastic ABI {L.elastic_abi_version()} != binding ABI {ABI_VERSION}")
+    return L
+
+
+lib = _load()
+
+
+def sparse_cfg(d: Optional[dict]) -> Optional[SparseCfg]:
+    """SparseCfg from a pattern dict: {"kind": "streaming", "sink", "window"} or
+    {"kind": "block", "block", "sink_blocks", "local_blocks", "stride_blocks"}."""
+    if d is None:
+        return None
+    if isinstance(d, SparseCfg):
+        return d
+    if d["kind"] == "streaming":
+        return SparseCfg(STREAMING, int(d["sink"]), int(d["window"]), 0, 0, 0, 0)
+    if d["kind"] == "block":
+        return SparseCfg(BLOCK, 0, 0, int(d["block"]), int(d["sink_blocks"]),
+                         int(d["local_blocks"]), int(d["stride_blocks"]))
+    raise ValueError(f"unknown sparse kind {d['kind']!r}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> C.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _check_dev(name, t, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _seq_args(cu_seqlens: Optional[torch.Tensor], total: int):
+    if cu_seqlens is None:
+        return 1
+    _check_dev("cu_seqlens", cu_seqlens, torch.int32)
+    return cu_seqlens.numel() - 1
+
+
+def route_workspace_size(batch: int, total_tokens: int, d_model: int) -> int:
+    return int(lib.elastic_route_workspace_size(batch, total_tokens, d_model))
+
+
+def route(hidden: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,
+          cu_seqlens: Optional[torch.Tensor] = None, threshold: float = 0.0,
+          pool_head: int = 0, pool_tail: int = 0, logits: Optional[torch.Tensor] = None,
+          mask: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+          stream=None):
+    """Attention Router on device: returns (logits [B, Hkv] fp32, mask [B, Hkv] int32)."""
+    _check_dev("hidden", hidden)
+    _check_dev("w1", w1, torch.float32)
+    _check_dev("w2", w2, torch.float32)
+    if hidden.dtype not in (torch.bfloat16, torch.float32) or hidden.dim() != 2:
+        raise ValueError("hidden must be a 2-D bf16 or fp32 tensor [T, d_model]")
+    T, d = hidden.shape
+    B = _seq_args(cu_seqlens, T)
+    dr, hkv = w1.shape[0], w2.shape[0]
+    if w1.shape != (dr, d) or w2.shape != (hkv, dr):
+        raise ValueError("w1 must be [d_router, d_model] and w2 [n_kv_heads, d_router]")
+    dev = hidden.device
+    if logits is None:
+        logits = torch.empty((B, hkv), dtype=torch.float32, device=dev)
+    if mask is None:
+        mask = torch.empty((B, hkv), dtype=torch.int32, device=dev)
+    _check_dev("logits", logits, torch.float32)
+    _check_dev("mask", mask, torch.int32)
+    need = route_workspace_size(B, T, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.elastic_route(_ptr(hidden), BF16 if hidden.dtype == torch.bfloat16 else FP32,
+                           _ptr(cu_seqlens), B, T, d, pool_head, pool_tail, _ptr(w1), dr,
+                           _ptr(w2), hkv, float(threshold), _ptr(logits), _ptr(mask),
+                           _ptr(workspace), workspace.numel() * workspace.element_size(),
+                           _stream(stream))
+    if st != OK:
+        raise ElasticError(st, "elastic_route")
+    return logits, mask
+
+
+def attn_workspace_size(dtype: int, batch: int, total_tokens: int, n_q_heads: int,
+                        n_kv_heads: int, head_dim: int) -> int:
+    return int(lib.elastic_attn_workspace_size(dtype, batch, total_tokens, n_q_heads, n_kv_heads,
+                                               head_dim))
+
+
+def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                 cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None,
+                 head_mask: Optional[torch.Tensor] = None, sparse=None,
+                 softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                 stream=None):
+    """Hybrid-head GQA prefill: returns o [T, Hq, D] (and fills ``lse`` [Hq, T] if given)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t)
+        if t.dim() != 3:
+            raise ValueError(f"{name} must be [T, heads, head_dim]")
+    if q.dtype not in (torch.bfloat16, torch.float32) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share dtype bf16 or fp32")
+    T, hq, D = q.shape
+    hkv = k.shape[1]
+    if k.shape != (T, hkv, D) or v.shape != (T, hkv, D):
+        raise ValueError("k and v must be [T, n_kv_heads, head_dim] matching q")
+    B = _seq_args(cu_seqlens, T)
+    dtype = BF16 if q.dtype == torch.bfloat16 else FP32
+    if out is None:
+        out = torch.empty_like(q)
+    _check_dev("out", out, q.dtype)
+    _check_dev("lse", lse, torch.float32)
+    _check_dev("head_mask", head_mask, torch.int32)
+    need = attn_workspace_size(dtype, B, T, hq, hkv, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    cfg = sparse_cfg(sparse)
+    st = lib.elastic_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), dtype, _ptr(cu_seqlens), B,
+                                  T, int(max_seqlen if max_seqlen is not None else T), hq, hkv, D,
+                                  float(softmax_scale), _ptr(head_mask),
+                                  C.byref(cfg) if cfg is not None else None, _ptr(lse),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(stream))
+    if st != OK:
+        raise ElasticError(st, "elastic_attn_prefill")
+    return out
+
+
+def attn_entries(seqlens, head_mask, n_q_heads: int, n_kv_heads: int, sparse=None) -> int:
+    """Allowed score entries over all query heads (host closed forms, no GPU involved)."""
+    lens = (C.c_int32 * len(seqlens))(*[int(x) for x in seqlens])
+    mask_arr = None
+    if head_mask is not None:
+        flat = [int(x) for row in head_mask for x in row]
+        mask_arr = (C.c_int32 * len(flat))(*flat)
+    cfg = sparse_cfg(sparse)
+    out = C.c_int64(0)
+    st = lib.elastic_attn_entries(lens, len(seqlens), mask_arr, n_q_heads, n_kv_heads,
+                                  C.byref(cfg) if cfg is not None else None, C.byref(out))
+    if st != OK:
+        raise ElasticError(st, "elastic_attn_entries")
+    return int(out.value)

@@ -1,0 +1,261 @@
+// C ABI of libelastic: argument validation, workspace layout and launch sequencing.
+// Every entry point validates on the host before touching HIP and never reads device memory,
+// so a call only enqueues work on the caller's stream.
+#include <stdio.h>
+#include <string.h>
+
+#include "elastic_internal.hpp"
+
+using namespace elastic;
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int hip_fail(hipError_t e, const char* where) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s", where, hipGetErrorString(e));
+  return ELASTIC_EHIP;
+}
+
+constexpr size_t ALIGN = 256;
+inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+// ---------------------------------------------------------------- attention sizing
+int attn_rows_per_item(int32_t dtype) { return dtype == ELASTIC_BF16 ? BF16_ROWS : F32_ROWS; }
+int attn_key_tile(int32_t dtype) { return dtype == ELASTIC_BF16 ? BF16_BK : F32_BK; }
+
+int64_t attn_max_items(int32_t dtype, int32_t batch, int64_t total_tokens, int32_t n_q_heads,
+                       int32_t n_kv_heads) {
+  const int G = n_q_heads / n_kv_heads;
+  const int BT = tokens_per_item(attn_rows_per_item(dtype), G);
+  return ((total_tokens + BT - 1) / BT + batch) * (int64_t)n_kv_heads;
+}
+
+struct AttnWorkspace {
+  size_t n_items, items, tile_prefix, total;
+};
+
+AttnWorkspace attn_layout(int64_t max_items, int32_t batch) {
+  AttnWorkspace w;
+  w.n_items = 0;
+  w.items = ALIGN;
+  w.tile_prefix = align_up(w.items + (size_t)max_items * sizeof(WorkItem));
+  w.total = align_up(w.tile_prefix + (size_t)(batch + 1) * sizeof(int32_t));
+  return w;
+}
+
+// ---------------------------------------------------------------- router sizing
+struct RouteWorkspace {
+  int64_t max_slabs;
+  size_t partials, pooled, z, total;
+};
+
+RouteWorkspace route_layout(int32_t batch, int64_t total_tokens, int32_t d_model) {
+  RouteWorkspace w;
+  w.max_slabs = (total_tokens + ROUTE_SLAB - 1) / ROUTE_SLAB + batch;
+  w.partials = 0;
+  w.pooled = align_up((size_t)w.max_slabs * d_model * sizeof(float));
+  w.z = align_up(w.pooled + (size_t)batch * d_model * sizeof(float));
+  w.total = align_up(w.z + (size_t)batch * ROUTE_MAX_DR * sizeof(float));
+  return w;
+}
+
+int check_pattern(const elastic_sparse_cfg* s) {
+  if (s->kind == ELASTIC_SPARSE_STREAMING) {
+    if (s->sink_tokens < 0 || s->window_tokens < 1) return ELASTIC_EINVAL;
+    return ELASTIC_OK;
+  }
+  if (s->kind == ELASTIC_SPARSE_BLOCK) {
+    if (s->sink_blocks < 0 || s->local_blocks < 0 || s->stride_blocks < 0) return ELASTIC_EINVAL;
+    if (s->block_size != 64 && s->block_size != 128) return ELASTIC_EUNSUPPORTED;
+    return ELASTIC_OK;
+  }
+  return ELASTIC_EINVAL;
+}
+
+Pattern to_pattern(const elastic_sparse_cfg* s) {
+  Pattern p{};
+  if (s == nullptr) {
+    p.kind = ELASTIC_SPARSE_STREAMING;
+    p.window = 1;
+    p.block = 64;
+    return p;
+  }
+  p.kind = s->kind;
+  p.sink = s->sink_tokens;
+  p.window = s->window_tokens;
+  p.block = s->block_size > 0 ? s->block_size : 64;
+  p.sink_blocks = s->sink_blocks;
+  p.local_blocks = s->local_blocks;
+  p.stride_blocks = s->stride_blocks;
+  return p;
+}
+
+// Allowed entries of one query head over a sequence of length n.
+int64_t head_entries(int64_t n, bool full, const elastic_sparse_cfg* s) {
+  if (n <= 0) return 0;
+  if (full) return n * (n + 1) / 2;
+  if (s->kind == ELASTIC_SPARSE_STREAMING) {
+    int64_t c = (int64_t)s->sink_tokens + s->window_tokens;
+    if (c > n) c = n;
+    return c * (c + 1) / 2 + (n - c) * c;
+  }
+  const int64_t B = s->block_size, stride = s->stride_blocks;
+  const int64_t nb = (n + B - 1) / B;
+  int64_t total = 0;
+  for (int64_t qb = 0; qb < nb; ++qb) {
+    // visible blocks strictly before qb: [0, a) U [bstart, qb) U {multiples of stride}
+    const int64_t a = s->sink_blocks < qb ? s->sink_blocks : qb;
+    int64_t bstart = qb - s->local_blocks;
+    if (bstart < 0) bstart = 0;
+    int64_t e;
+    if (a >= bstart) {
+      e = qb;
+    } else {
+      e = a + (qb - bstart);
+      if (stride > 0) e += (bstart + stride - 1) / stride - (a + stride - 1) / stride;
+    }
+    const int64_t r0 = qb * B;
+    const int64_t nr = (r0 + B < n ? r0 + B : n) - r0;
+    total += nr * e * B + nr * (nr + 1) / 2;
+  }
+  return total;
+}
+
+}  // namespace
+
+extern "C" {
+
+int elastic_abi_version(void) { return ELASTIC_ABI_VERSION; }
+
+const char* elastic_status_string(int status) {
+  switch (status) {
+    case ELASTIC_OK: return "ok";
+    case ELASTIC_EINVAL: return "invalid argument";
+    case ELASTIC_EUNSUPPORTED: return "unsupported configuration";
+    case ELASTIC_EWORKSPACE: return "workspace too small";
+    case ELASTIC_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* elastic_last_error(void) { return g_last_error; }
+
+size_t elastic_route_workspace_size(int32_t batch, int64_t total_tokens, int32_t d_model) {
+  if (batch < 1 || total_tokens < 0 || d_model < 1) return 0;
+  return route_layout(batch, total_tokens, d_model).total;
+}
+
+int elastic_route(const void* hidden, int32_t hidden_dtype, const int32_t* cu_seqlens,
+                  int32_t batch, int64_t total_tokens, int32_t d_model, int32_t pool_head,
+                  int32_t pool_tail, const float* w1, int32_t d_router, const float* w2,
+                  int32_t n_kv_heads, float threshold, float* logits_out, int32_t* mask_out,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (w1 == nullptr || w2 == nullptr || mask_out == nullptr) return ELASTIC_EINVAL;
+  if (hidden == nullptr && total_tokens > 0) return ELASTIC_EINVAL;
+  if (batch < 1 || total_tokens < 0 || total_tokens > INT32_MAX) return ELASTIC_EINVAL;
+  if (cu_seqlens == nullptr && batch != 1) return ELASTIC_EINVAL;
+  if (pool_head < 0 || pool_tail < 0) return ELASTIC_EINVAL;
+  if (d_model < 1 || d_router < 1 || n_kv_heads < 1) return ELASTIC_EINVAL;
+  if (hidden_dtype != ELASTIC_BF16 && hidden_dtype != ELASTIC_FP32) return ELASTIC_EUNSUPPORTED;
+  if (d_model % 8 != 0 || d_router > ROUTE_MAX_DR || n_kv_heads > ROUTE_MAX_HKV)
+    return ELASTIC_EUNSUPPORTED;
+  const RouteWorkspace lay = route_layout(batch, total_tokens, d_model);
+  if (workspace == nullptr || workspace_bytes < lay.total) return ELASTIC_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  const hipError_t e = launch_route(
+      hidden, hidden_dtype, cu_seqlens, batch, total_tokens, d_model, pool_head, pool_tail, w1,
+      d_router, w2, n_kv_heads, threshold, logits_out, mask_out,
+      reinterpret_cast<float*>(ws + lay.partials), total_tokens > 0 ? lay.max_slabs : 0,
+      reinterpret_cast<float*>(ws + lay.pooled), reinterpret_cast<float*>(ws + lay.z),
+      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ELASTIC_OK : hip_fail(e, "elastic_route");
+}
+
+size_t elastic_attn_workspace_size(int32_t dtype, int32_t batch, int64_t total_tokens,
+                                   int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim) {
+  (void)head_dim;
+  if ((dtype != ELASTIC_BF16 && dtype != ELASTIC_FP32) || batch < 1 || total_tokens < 0 ||
+      n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads != 0 ||
+      n_q_heads / n_kv_heads > attn_rows_per_item(dtype))
+    return 0;
+  return attn_layout(attn_max_items(dtype, batch, total_tokens, n_q_heads, n_kv_heads), batch).total;
+}
+
+int elastic_attn_prefill(const void* q, const void* k, const void* v, void* o, int32_t dtype,
+                         const int32_t* cu_seqlens, int32_t batch, int64_t total_tokens,
+                         int32_t max_seqlen, int32_t n_q_heads, int32_t n_kv_heads,
+                         int32_t head_dim, float softmax_scale, const int32_t* head_mask,
+                         const elastic_sparse_cfg* sparse, float* lse_out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (batch < 1 || total_tokens < 0 || total_tokens > INT32_MAX || max_seqlen < 0)
+    return ELASTIC_EINVAL;
+  if (total_tokens > 0 && (q == nullptr || k == nullptr || v == nullptr || o == nullptr))
+    return ELASTIC_EINVAL;
+  if (cu_seqlens == nullptr && batch != 1) return ELASTIC_EINVAL;
+  if (n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads != 0) return ELASTIC_EINVAL;
+  if (head_mask != nullptr && sparse == nullptr) return ELASTIC_EINVAL;
+  if (sparse != nullptr) {
+    const int st = check_pattern(sparse);
+    if (st != ELASTIC_OK) return st;
+  }
+  if (dtype != ELASTIC_BF16 && dtype != ELASTIC_FP32) return ELASTIC_EUNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return ELASTIC_EUNSUPPORTED;
+  if (n_q_heads / n_kv_heads > attn_rows_per_item(dtype)) return ELASTIC_EUNSUPPORTED;
+  const int64_t max_items = attn_max_items(dtype, batch, total_tokens, n_q_heads, n_kv_heads);
+  if (max_items > INT32_MAX) return ELASTIC_EUNSUPPORTED;
+  const AttnWorkspace lay = attn_layout(max_items, batch);
+  if (workspace == nullptr || workspace_bytes < lay.total) return ELASTIC_EWORKSPACE;
+  if (total_tokens == 0) return ELASTIC_OK;
+
+  const int G = n_q_heads / n_kv_heads;
+  const int BT = tokens_per_item(attn_rows_per_item(dtype), G);
+  const int BK = attn_key_tile(dtype);
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
+  const Pattern pat = to_pattern(sparse);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* n_items = reinterpret_cast<int32_t*>(ws + lay.n_items);
+  WorkItem* items = reinterpret_cast<WorkItem*>(ws + lay.items);
+  int32_t* tile_prefix = reinterpret_cast<int32_t*>(ws + lay.tile_prefix);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+
+  hipError_t e = launch_plan(cu_seqlens, batch, total_tokens, n_kv_heads, head_mask, pat, BT, BK,
+                             max_items, tile_prefix, items, n_items, st);
+  if (e != hipSuccess) return hip_fail(e, "elastic_attn_prefill: plan");
+  if (dtype == ELASTIC_BF16)
+    e = launch_attn_bf16(head_dim, q, k, v, o, lse_out, cu_seqlens, total_tokens, n_q_heads,
+                         n_kv_heads, BT, scale, head_mask, pat, items, n_items, max_items, st);
+  else
+    e = launch_attn_f32(head_dim, q, k, v, o, lse_out, cu_seqlens, total_tokens, n_q_heads,
+                        n_kv_heads, BT, scale, head_mask, pat, items, n_items, max_items, st);
+  if (e != hipSuccess) return hip_fail(e, "elastic_attn_prefill: attention");
+  return ELASTIC_OK;
+}
+
+int elastic_attn_entries(const int32_t* seqlens_host, int32_t batch,
+                         const int32_t* head_mask_host, int32_t n_q_heads, int32_t n_kv_heads,
+                         const elastic_sparse_cfg* sparse, int64_t* entries_out) {
+  if (seqlens_host == nullptr || entries_out == nullptr || batch < 1) return ELASTIC_EINVAL;
+  if (n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads != 0) return ELASTIC_EINVAL;
+  if (head_mask_host != nullptr && sparse == nullptr) return ELASTIC_EINVAL;
+  if (sparse != nullptr) {
+    const int st = check_pattern(sparse);
+    if (st != ELASTIC_OK) return st;
+  }
+  const int64_t G = n_q_heads / n_kv_heads;
+  int64_t total = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    if (seqlens_host[b] < 0) return ELASTIC_EINVAL;
+    int64_t full_e = -1, sparse_e = -1;
+    for (int32_t g = 0; g < n_kv_heads; ++g) {
+      const bool full = head_mask_host == nullptr || head_mask_host[(int64_t)b * n_kv_heads + g] != 0;
+      int64_t& slot = full ? full_e : sparse_e;
+      if (slot < 0) slot = head_entries(seqlens_host[b], full, sparse);
+      total += G * slot;
+    }
+  }
+  *entries_out = total;
+  return ELASTIC_OK;
+}
+
+}  // extern "C"

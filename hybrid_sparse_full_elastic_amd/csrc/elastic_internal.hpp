@@ -1,0 +1,155 @@
+// Internal declarations of libelastic (gfx950).  Not part of the public ABI.
+//
+// Key-tile geometry shared by the scheduler and the attention kernels.  Positions are local
+// to a sequence.  A work item is (sequence, KV head, query tile of BT tokens); it visits the
+// key tiles (BK keys each) that hold at least one key some query of the tile may see, in
+// increasing order.  Mode rules follow "Elastic Attention" (arXiv 2601.17367; paperlayer
+// summary, section 2 "Hybrid Head Mechanism", appendix D.1 "Sparse Inference"): full heads
+// are causal; sparse heads use sink + local window streaming or a fixed block pattern.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/elastic.h"
+
+namespace elastic {
+
+enum : int { MODE_STREAM = ELASTIC_SPARSE_STREAMING, MODE_BLOCK = ELASTIC_SPARSE_BLOCK, MODE_FULL = 2 };
+
+// Sparse pattern as the kernels see it (by value in kernel arguments).
+struct Pattern {
+  int kind;                  // ELASTIC_SPARSE_*
+  int sink, window;          // streaming
+  int block, sink_blocks, local_blocks, stride_blocks;
+};
+
+// One scheduled unit of attention work.
+struct WorkItem {
+  int seq;    // sequence index b
+  int group;  // KV head g
+  int qtile;  // query tile index: tokens [qtile * BT, min(n, (qtile + 1) * BT))
+  int cost;   // key tiles visited (scheduling weight)
+};
+
+// Is key j visible to query i (local positions) under `mode`?
+__host__ __device__ inline bool key_allowed(int mode, const Pattern& p, int i, int j) {
+  if (j > i) return false;
+  if (mode == MODE_FULL) return true;
+  if (mode == MODE_STREAM) return j < p.sink || i - j < p.window;
+  const int qb = i / p.block, kb = j / p.block;
+  return kb < p.sink_blocks || qb - kb <= p.local_blocks ||
+         (p.stride_blocks > 0 && kb % p.stride_blocks == 0);
+}
+
+// Key tiles visited by the query tokens [t0, t1] (inclusive) of one work item.
+struct KeyTiles {
+  int mode, BK, t0, t1, last;
+  Pattern p;
+  int sink_end, win_begin;  // streaming: tiles [0, sink_end) and [win_begin, last]
+  int tpb, qb0, qb1;        // block: tiles per block, query blocks of t0 and t1
+
+  __host__ __device__ KeyTiles(int mode_, const Pattern& p_, int t0_, int t1_, int BK_)
+      : mode(mode_), BK(BK_), t0(t0_), t1(t1_), last(t1_ / BK_), p(p_) {
+    sink_end = 0;
+    win_begin = 0;
+    tpb = 1;
+    qb0 = qb1 = 0;
+    if (mode == MODE_STREAM) {
+      const int sink_keys = p.sink < t1 + 1 ? p.sink : t1 + 1;
+      sink_end = (sink_keys + BK - 1) / BK;
+      const int w0 = t0 - p.window + 1;
+      win_begin = w0 > 0 ? w0 / BK : 0;
+    } else if (mode == MODE_BLOCK) {
+      tpb = p.block / BK;  // block_size is a multiple of BK (checked on the host)
+      qb0 = t0 / p.block;
+      qb1 = t1 / p.block;
+    }
+  }
+
+  // Smallest key block >= kb that some query block in [qb0, qb1] may see.
+  __host__ __device__ int next_block(int kb) const {
+    if (kb < p.sink_blocks || kb >= qb0 - p.local_blocks) return kb;
+    int c = qb0 - p.local_blocks;
+    if (p.stride_blocks > 0) {
+      const int m = ((kb + p.stride_blocks - 1) / p.stride_blocks) * p.stride_blocks;
+      if (m < c) c = m;
+    }
+    return c;
+  }
+
+  // Smallest visited tile >= kt, or -1 when there is none.
+  __host__ __device__ int next(int kt) const {
+    if (kt > last) return -1;
+    if (mode == MODE_STREAM) {
+      if (kt >= sink_end && kt < win_begin) kt = win_begin;
+    } else if (mode == MODE_BLOCK) {
+      const int kb = kt / tpb;
+      const int nb = next_block(kb);
+      if (nb != kb) kt = nb * tpb;
+    }
+    return kt <= last ? kt : -1;
+  }
+
+  // Does tile kt need per-element masking for some (query, key) pair of this item?
+  __host__ __device__ bool needs_mask(int kt) const {
+    const int k0 = kt * BK, k1 = k0 + BK - 1;
+    if (k1 > t0) return true;  // causal edge (also covers keys past the sequence end)
+    if (mode == MODE_FULL) return false;
+    if (mode == MODE_STREAM) return !(k1 < p.sink || k0 > t1 - p.window);
+    const int kb = k0 / p.block;
+    return !(kb < p.sink_blocks || kb >= qb1 - p.local_blocks ||
+             (p.stride_blocks > 0 && kb % p.stride_blocks == 0));
+  }
+
+  __host__ __device__ int count() const {
+    if (mode == MODE_FULL) return last + 1;
+    int c = 0;
+    for (int kt = next(0); kt >= 0; kt = next(kt + 1)) ++c;
+    return c;
+  }
+};
+
+// ------------------------------------------------------------------ tile configurations
+// bf16 MFMA attention: NW waves x NB blocks of 32 query rows per workgroup, 64-key tiles.
+constexpr int BF16_NW = 4;
+constexpr int BF16_NB = 2;
+constexpr int BF16_ROWS = BF16_NW * BF16_NB * 32;  // query rows (token, head) per workgroup
+constexpr int BF16_BK = 64;
+// fp32 attention: one thread per query row, 32-key tiles.
+constexpr int F32_ROWS = 256;
+constexpr int F32_BK = 32;
+
+// Query tokens per work item: the workgroup's rows hold whole tokens' G heads.
+inline int tokens_per_item(int rows, int G) { return rows / G; }
+
+// ------------------------------------------------------------------ launchers (device code)
+hipError_t launch_plan(const int32_t* cu_seqlens, int batch, int64_t total_tokens, int n_kv_heads,
+                       const int32_t* head_mask, const Pattern& pat, int BT, int BK,
+                       int64_t max_items, int32_t* tile_prefix, WorkItem* items, int32_t* n_items,
+                       hipStream_t stream);
+
+hipError_t launch_attn_bf16(int head_dim, const void* q, const void* k, const void* v, void* o,
+                            float* lse, const int32_t* cu_seqlens, int64_t total_tokens,
+                            int n_q_heads, int n_kv_heads, int BT, float scale,
+                            const int32_t* head_mask, const Pattern& pat, const WorkItem* items,
+                            const int32_t* n_items, int64_t grid, hipStream_t stream);
+
+hipError_t launch_attn_f32(int head_dim, const void* q, const void* k, const void* v, void* o,
+                           float* lse, const int32_t* cu_seqlens, int64_t total_tokens,
+                           int n_q_heads, int n_kv_heads, int BT, float scale,
+                           const int32_t* head_mask, const Pattern& pat, const WorkItem* items,
+                           const int32_t* n_items, int64_t grid, hipStream_t stream);
+
+// Router: rows of sequence b are pooled in slabs of ROUTE_SLAB rows.
+constexpr int ROUTE_SLAB = 128;
+constexpr int ROUTE_MAX_DR = 256;   // d_router limit
+constexpr int ROUTE_MAX_HKV = 256;  // n_kv_heads limit
+
+hipError_t launch_route(const void* hidden, int hidden_dtype, const int32_t* cu_seqlens, int batch,
+                        int64_t total_tokens, int d_model, int pool_head, int pool_tail,
+                        const float* w1, int d_router, const float* w2, int n_kv_heads,
+                        float threshold, float* logits_out, int32_t* mask_out, float* partials,
+                        int64_t max_slabs, float* pooled, float* zbuf, hipStream_t stream);
+
+}  // namespace elastic

@@ -1,0 +1,131 @@
+// Scheduler: turns (sequence, KV head, query tile) units and the device-resident head mask
+// into one work list, heaviest first, for the single hybrid attention launch.
+//
+// The pages describe the deployment problem this solves: mixed full and sparse heads are
+// slow when run as separate passes on one GPU, so routing metadata goes straight into one
+// unified launch without splitting tensors ("Elastic Attention", arXiv 2601.17367;
+// paperlayer summary, section 3 "Efficient Deployment" and appendix D.1 "Sparse
+// Inference").  Here the mask never leaves the device: one workgroup reads it, costs every
+// item by the number of key tiles it visits (O(n) for full items, O(sink + window) for
+// streaming ones), and counting-sorts the items by decreasing cost (longest processing time
+// first), so the hardware dispatcher hands the long causal items out first and the short
+// sparse items fill the tail.
+#include "elastic_internal.hpp"
+
+namespace elastic {
+namespace {
+
+constexpr int PLAN_THREADS = 1024;
+constexpr int PLAN_BUCKETS = 4096;  // costs >= PLAN_BUCKETS - 1 share the last bucket
+
+__device__ inline int seq_len(const int32_t* cu, int b, int64_t total) {
+  return cu ? cu[b + 1] - cu[b] : (int)total;
+}
+
+__global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
+    const int32_t* __restrict__ cu_seqlens, int batch, int64_t total_tokens, int n_kv_heads,
+    const int32_t* __restrict__ head_mask, Pattern pat, int BT, int BK, int64_t max_items,
+    int32_t* __restrict__ tile_prefix, WorkItem* __restrict__ items, int32_t* __restrict__ n_items) {
+  __shared__ int hist[PLAN_BUCKETS];
+  __shared__ int cursor[PLAN_BUCKETS];
+  __shared__ int scan_tmp[PLAN_THREADS];
+  __shared__ int carry;
+  const int tid = threadIdx.x;
+
+  // 1. tile_prefix[b] = query tiles of sequences before b (block-wide scan in chunks).
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < batch; base += PLAN_THREADS) {
+    const int b = base + tid;
+    const int nt = b < batch ? (seq_len(cu_seqlens, b, total_tokens) + BT - 1) / BT : 0;
+    scan_tmp[tid] = nt;
+    __syncthreads();
+    for (int off = 1; off < PLAN_THREADS; off <<= 1) {
+      const int add = tid >= off ? scan_tmp[tid - off] : 0;
+      __syncthreads();
+      scan_tmp[tid] += add;
+      __syncthreads();
+    }
+    if (b < batch) tile_prefix[b] = carry + scan_tmp[tid] - nt;
+    __syncthreads();
+    if (tid == PLAN_THREADS - 1) carry += scan_tmp[tid];
+    __syncthreads();
+  }
+  const int total_tiles = carry;
+  if (tid == 0) tile_prefix[batch] = total_tiles;
+  int64_t count = (int64_t)total_tiles * n_kv_heads;
+  if (count > max_items) count = max_items;  // cannot happen for consistent cu_seqlens
+  const int nitem = (int)count;
+
+  for (int i = tid; i < PLAN_BUCKETS; i += PLAN_THREADS) {
+    hist[i] = 0;
+    cursor[i] = 0;
+  }
+  __syncthreads();
+
+  // 2. Enumerate items u = tile * n_kv_heads + g, cost each and histogram the costs.
+  auto describe = [&](int u, WorkItem& it) {
+    const int tile = u / n_kv_heads;
+    const int g = u - tile * n_kv_heads;
+    int lo = 0, hi = batch - 1;  // last b with tile_prefix[b] <= tile
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tile_prefix[mid] <= tile) lo = mid; else hi = mid - 1;
+    }
+    const int b = lo;
+    const int qt = tile - tile_prefix[b];
+    const int n = seq_len(cu_seqlens, b, total_tokens);
+    const int t0 = qt * BT;
+    const int t1 = min(t0 + BT, n) - 1;
+    const bool full = head_mask == nullptr || head_mask[b * n_kv_heads + g] != 0;
+    KeyTiles kt(full ? MODE_FULL : pat.kind, pat, t0, t1, BK);
+    it.seq = b;
+    it.group = g;
+    it.qtile = qt;
+    it.cost = kt.count();
+  };
+  __threadfence_block();
+  for (int u = tid; u < nitem; u += PLAN_THREADS) {
+    WorkItem it;
+    describe(u, it);
+    const int bucket = min(it.cost, PLAN_BUCKETS - 1);
+    atomicAdd(&hist[bucket], 1);
+  }
+  __syncthreads();
+
+  // 3. Exclusive scan in decreasing-cost order: offset[c] = items with bucket > c.
+  if (tid == 0) {
+    int run = 0;
+    for (int c = PLAN_BUCKETS - 1; c >= 0; --c) {
+      const int h = hist[c];
+      hist[c] = run;
+      run += h;
+    }
+  }
+  __syncthreads();
+
+  // 4. Scatter.  Order inside a bucket is arbitrary; every item writes disjoint outputs with
+  //    a fixed reduction order, so results do not depend on it.
+  for (int u = tid; u < nitem; u += PLAN_THREADS) {
+    WorkItem it;
+    describe(u, it);
+    const int bucket = min(it.cost, PLAN_BUCKETS - 1);
+    const int pos = hist[bucket] + atomicAdd(&cursor[bucket], 1);
+    items[pos] = it;
+  }
+  if (tid == 0) *n_items = nitem;
+}
+
+}  // namespace
+
+hipError_t launch_plan(const int32_t* cu_seqlens, int batch, int64_t total_tokens, int n_kv_heads,
+                       const int32_t* head_mask, const Pattern& pat, int BT, int BK,
+                       int64_t max_items, int32_t* tile_prefix, WorkItem* items, int32_t* n_items,
+                       hipStream_t stream) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, cu_seqlens, batch,
+                     total_tokens, n_kv_heads, head_mask, pat, BT, BK, max_items, tile_prefix,
+                     items, n_items);
+  return hipGetLastError();
+}
+
+}  // namespace elastic

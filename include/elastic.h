@@ -1,0 +1,164 @@
+/*
+ * elastic.h - C ABI of libelastic: Elastic Attention prefill on AMD Instinct MI355X (gfx950).
+ *
+ * Method: "Elastic Attention: Test-time Adaptive Sparsity Ratios for Efficient Transformers"
+ * (arXiv 2601.17367), as summarised on paperlayer.ai (abs/2601.17367v2).  An Attention
+ * Router reads a layer's hidden states and gives every key/value head a binary choice
+ * between full attention and sparse attention (summary section 3, "Attention Router");
+ * heads then run in one hybrid launch and their outputs are concatenated (section 2,
+ * "Hybrid Head Mechanism"; appendix D.1, "Sparse Inference": routing metadata goes
+ * straight to one unified kernel launch).
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller, unless a comment says
+ *    "host".  The library never allocates, frees or synchronises; each call only enqueues
+ *    work on `stream` (a hipStream_t; NULL = the null stream) and returns.
+ *  - Layouts are dense, row-major and token-major: q and o are [T, Hq, D], k and v are
+ *    [T, Hkv, D], hidden is [T, d_model].  Sequences of a batch are packed back to back;
+ *    `cu_seqlens` (device, int32 [batch+1], cu_seqlens[0] = 0, non-decreasing,
+ *    cu_seqlens[batch] = total_tokens) gives their offsets.  cu_seqlens == NULL is allowed
+ *    only with batch == 1 and means one sequence of total_tokens tokens.
+ *  - Positions are local to a sequence; no token attends across sequences.
+ *  - Query head h reads key/value head h / G with G = Hq / Hkv (grouped-query attention)
+ *    and takes that head's full/sparse mode: the router decides per key/value head.
+ *  - Arguments are validated on the host before any HIP call; a failure returns
+ *    ELASTIC_EINVAL / ELASTIC_EUNSUPPORTED / ELASTIC_EWORKSPACE and enqueues nothing.
+ *    Device-resident values (cu_seqlens, head masks) are never read on the host, so the
+ *    caller must pass consistent ones; a launch error returns ELASTIC_EHIP and
+ *    elastic_last_error() gives the HIP message (thread-local).
+ *  - Concurrent calls are safe when each uses its own workspace; calls that share a
+ *    workspace must be ordered on one stream.
+ */
+#ifndef ELASTIC_H_
+#define ELASTIC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ELASTIC_ABI_VERSION 1
+
+enum elastic_status {
+  ELASTIC_OK = 0,
+  ELASTIC_EINVAL = 1,       /* null required pointer, non-positive size, inconsistent shapes */
+  ELASTIC_EUNSUPPORTED = 2, /* valid but not implemented: head_dim, dtype, pattern geometry */
+  ELASTIC_EWORKSPACE = 3,   /* workspace_bytes below the matching *_workspace_size() */
+  ELASTIC_EHIP = 4          /* a HIP launch or runtime call failed */
+};
+
+enum elastic_dtype { ELASTIC_BF16 = 0, ELASTIC_FP32 = 1 };
+
+enum elastic_sparse_kind {
+  /* Streaming sparse attention (summary section 4 and appendix B.2; appendix D.1 gives
+   * 128 sink tokens): query i sees key j <= i iff j < sink_tokens or i - j < window_tokens
+   * (the window counts the query itself), so it sees min(i + 1, sink + window) keys. */
+  ELASTIC_SPARSE_STREAMING = 0,
+  /* Fixed block-sparse pattern (appendix D.1, "unified block-sparse kernel"): with
+   * qb = i / block_size and kb = j / block_size, query i sees key j <= i iff
+   * kb < sink_blocks, or qb - kb <= local_blocks, or (stride_blocks > 0 and
+   * kb % stride_blocks == 0).  Blocks strictly below the diagonal are fully visible; the
+   * diagonal block is causal inside. */
+  ELASTIC_SPARSE_BLOCK = 1
+};
+
+/* Pattern of the sparse heads.  Read on the host during the call only. */
+typedef struct elastic_sparse_cfg {
+  int32_t kind;          /* enum elastic_sparse_kind */
+  int32_t sink_tokens;   /* streaming: >= 0 */
+  int32_t window_tokens; /* streaming: >= 1 */
+  int32_t block_size;    /* block: 64 or 128 */
+  int32_t sink_blocks;   /* block: >= 0 */
+  int32_t local_blocks;  /* block: >= 0 (blocks strictly before the diagonal block) */
+  int32_t stride_blocks; /* block: >= 0, 0 = no strided blocks */
+} elastic_sparse_cfg;
+
+/* ABI version compiled into the library (ELASTIC_ABI_VERSION). */
+int elastic_abi_version(void);
+
+/* Static text for a status code. */
+const char* elastic_status_string(int status);
+
+/* Text of the last ELASTIC_EHIP error on the calling thread ("" if none). */
+const char* elastic_last_error(void);
+
+/* Bytes of workspace elastic_route needs for these sizes (device memory, any alignment
+ * of at least 256 bytes; contents need not be initialised). */
+size_t elastic_route_workspace_size(int32_t batch, int64_t total_tokens, int32_t d_model);
+
+/*
+ * Attention Router forward (summary section 1: the router reads the input hidden states
+ * and routes per head; section 3 "Attention Router": pooled hidden states, a task MLP and
+ * a router MLP give head-wise logits that pick full or sparse attention; appendix H.4
+ * "Router Input Length": boundary pooling of the first and last tokens).
+ *
+ * For every sequence b:  h = mean of hidden rows of b (all rows when pool_head ==
+ * pool_tail == 0; otherwise the first pool_head and last pool_tail rows, each row at most
+ * once), z = W1 h, a = max(z, 0), logit = W2 a, mask = (logit > threshold).
+ *
+ *  hidden      [total_tokens, d_model], dtype hidden_dtype (ELASTIC_BF16 or ELASTIC_FP32)
+ *  w1          [d_router, d_model] fp32 row-major;   d_router in [1, 256]
+ *  w2          [n_kv_heads, d_router] fp32 row-major; n_kv_heads in [1, 256]
+ *  logits_out  [batch, n_kv_heads] fp32, may be NULL
+ *  mask_out    [batch, n_kv_heads] int32, 1 = full attention, 0 = sparse (required)
+ *  d_model     multiple of 8.  Sums are fp32 in a fixed order: results are bitwise
+ *              reproducible run to run.  A sequence of length 0 pools nothing: its
+ *              logits are 0 and its mask is all sparse.
+ */
+int elastic_route(const void* hidden, int32_t hidden_dtype, const int32_t* cu_seqlens,
+                  int32_t batch, int64_t total_tokens, int32_t d_model, int32_t pool_head,
+                  int32_t pool_tail, const float* w1, int32_t d_router, const float* w2,
+                  int32_t n_kv_heads, float threshold, float* logits_out, int32_t* mask_out,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace elastic_attn_prefill needs (device memory, 256-byte aligned). */
+size_t elastic_attn_workspace_size(int32_t dtype, int32_t batch, int64_t total_tokens,
+                                   int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim);
+
+/*
+ * Hybrid-head GQA prefill attention in one scheduled launch (summary section 2 "Hybrid
+ * Head Mechanism"; section 3 "Efficient Deployment": one fused kernel computes retrieval
+ * (full) and sparse heads on a single GPU; appendix D.1: routing metadata is passed
+ * directly to one launch without splitting tensors).
+ *
+ * For query head h of sequence b with key/value head g = h / G:
+ *   mode = head_mask[b * n_kv_heads + g] != 0 ? full causal : the `sparse` pattern,
+ *   o[i, h, :] = sum_{j in A(i)} softmax_j(scale * <q_i, k_j>) v_j,
+ *   lse[h, i]  = log sum_{j in A(i)} exp(scale * <q_i, k_j>)      (natural log)
+ *
+ *  q, o        [total_tokens, n_q_heads, head_dim]   dtype (bf16 or fp32; o same dtype)
+ *  k, v        [total_tokens, n_kv_heads, head_dim]
+ *  head_mask   [batch, n_kv_heads] int32 (router output or a forced mask); NULL = all full
+ *  sparse      host pointer, pattern of the sparse heads (required unless head_mask NULL)
+ *  lse_out     [n_q_heads, total_tokens] fp32, may be NULL
+ *  softmax_scale <= 0 selects head_dim^-1/2.
+ *  max_seqlen  >= every sequence length (used for sizing only).
+ * Supported: head_dim 64 or 128; bf16 (bf16 MFMA, fp32 accumulation and softmax) or fp32
+ * (fp32 throughout); n_q_heads % n_kv_heads == 0.
+ */
+int elastic_attn_prefill(const void* q, const void* k, const void* v, void* o, int32_t dtype,
+                         const int32_t* cu_seqlens, int32_t batch, int64_t total_tokens,
+                         int32_t max_seqlen, int32_t n_q_heads, int32_t n_kv_heads,
+                         int32_t head_dim, float softmax_scale, const int32_t* head_mask,
+                         const elastic_sparse_cfg* sparse, float* lse_out, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * Host-only work counter (no HIP call): the number of allowed (query, key) score entries
+ * over all query heads, for sequences of the given lengths (host int32 [batch]) and head
+ * modes (host int32 [batch, n_kv_heads], NULL = all full).  Effective attention FLOPs are
+ * 4 * head_dim * entries.  Closed forms: full n(n+1)/2 per head; streaming
+ * c(c+1)/2 + (n-c)c with c = min(n, sink+window); block: per query block, the visible
+ * earlier blocks times block_size plus the causal diagonal block.
+ */
+int elastic_attn_entries(const int32_t* seqlens_host, int32_t batch,
+                         const int32_t* head_mask_host, int32_t n_q_heads, int32_t n_kv_heads,
+                         const elastic_sparse_cfg* sparse, int64_t* entries_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ELASTIC_H_ */

@@ -215,10 +215,9 @@ def sample_rows(seqlen: int, reach: int, block: int = 128, every: int = 16) -> n
 
 
 def spread_rows(seqlen: int, count: int, seed: int = 0) -> np.ndarray:
-    """``count`` distinct rows: the first and last rows plus a seeded uniform spread."""
+    """Sorted distinct rows of one sequence: a seeded uniform draw of ``count`` rows plus the
+    first and the last row."""
     rng = np.random.default_rng([seed, 99])
-    count = min(count, seqlen)
-    base = {0, seqlen - 1}
-    extra = rng.choice(seqlen, size=count, replace=False)
-    rows = sorted(base.union(int(x) for x in extra))
-    return np.array(rows[:max(count, 2)], dtype=np.int64)
+    rows = set(rng.choice(seqlen, size=min(count, seqlen), replace=False).tolist())
+    rows.update({0, seqlen - 1})
+    return np.array(sorted(rows), dtype=np.int64)

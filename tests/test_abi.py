@@ -1,0 +1,141 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every declared symbol,
+rejects invalid arguments on the host before any HIP call, sizes its workspaces
+monotonically, and its host-side entry counter agrees with the oracle's enumeration."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import inputs as syn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "elastic.h")
+
+ext = pytest.importorskip("hybrid_sparse_full_elastic_amd", reason="libelastic.so not built")
+L = ext.lib
+FAKE = C.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(elastic_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    syms = declared_symbols()
+    assert {"elastic_route", "elastic_attn_prefill", "elastic_attn_entries"} <= set(syms)
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def test_version_and_status_strings():
+    assert L.elastic_abi_version() == ext.ABI_VERSION
+    for st in range(5):
+        assert L.elastic_status_string(st).decode() not in ("", "unknown status")
+    assert L.elastic_status_string(99).decode() == "unknown status"
+
+
+def _attn(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dtype=0, cu=None, batch=1, T=256, maxlen=256, hq=8,
+             hkv=2, D=128, scale=0.0, mask=None, sparse=ext.sparse_cfg({"kind": "streaming", "sink": 4, "window": 64}),
+             lse=None, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    sp = C.byref(a["sparse"]) if a["sparse"] is not None else None
+    return L.elastic_attn_prefill(a["q"], a["k"], a["v"], a["o"], a["dtype"], a["cu"], a["batch"],
+                                  a["T"], a["maxlen"], a["hq"], a["hkv"], a["D"], a["scale"],
+                                  a["mask"], sp, a["lse"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_attention_validation_without_gpu():
+    EINVAL, EUNS, EWS = 1, 2, 3
+    assert _attn(q=None) == EINVAL
+    assert _attn(o=None) == EINVAL
+    assert _attn(batch=0) == EINVAL
+    assert _attn(batch=2, cu=None) == EINVAL
+    assert _attn(hq=6, hkv=4) == EINVAL
+    assert _attn(T=-1) == EINVAL
+    assert _attn(mask=FAKE, sparse=None) == EINVAL
+    assert _attn(D=96) == EUNS
+    assert _attn(dtype=7) == EUNS
+    assert _attn(hq=512, hkv=1) == EUNS
+    assert _attn(sparse=ext.sparse_cfg({"kind": "streaming", "sink": 4, "window": 0})) == EINVAL
+    assert _attn(sparse=ext.sparse_cfg({"kind": "streaming", "sink": -1, "window": 8})) == EINVAL
+    bad_kind = ext.SparseCfg(9, 0, 1, 0, 0, 0, 0)
+    assert _attn(sparse=bad_kind) == EINVAL
+    blk = {"kind": "block", "block": 96, "sink_blocks": 1, "local_blocks": 8, "stride_blocks": 16}
+    assert _attn(sparse=ext.sparse_cfg(blk)) == EUNS
+    assert _attn(ws=None) == EWS
+    need = ext.attn_workspace_size(0, 1, 256, 8, 2, 128)
+    assert need > 0
+    assert _attn(wsb=need - 1) == EWS
+    assert _attn(T=0, q=None, k=None, v=None, o=None, wsb=need) == 0  # empty input: no-op
+
+
+def _route(**kw):
+    a = dict(hidden=FAKE, dtype=0, cu=None, batch=1, T=1024, d=4096, ph=0, pt=0, w1=FAKE, dr=64,
+             w2=FAKE, hkv=8, thr=0.0, logits=None, mask=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return L.elastic_route(a["hidden"], a["dtype"], a["cu"], a["batch"], a["T"], a["d"], a["ph"],
+                           a["pt"], a["w1"], a["dr"], a["w2"], a["hkv"], a["thr"], a["logits"],
+                           a["mask"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_route_validation_without_gpu():
+    EINVAL, EUNS, EWS = 1, 2, 3
+    assert _route(w1=None) == EINVAL
+    assert _route(mask=None) == EINVAL
+    assert _route(hidden=None) == EINVAL
+    assert _route(batch=3) == EINVAL
+    assert _route(ph=-1) == EINVAL
+    assert _route(d=4100) == EUNS
+    assert _route(dr=300) == EUNS
+    assert _route(hkv=257) == EUNS
+    assert _route(dtype=5) == EUNS
+    assert _route(ws=None) == EWS
+    need = ext.route_workspace_size(1, 1024, 4096)
+    assert _route(wsb=need - 1) == EWS
+
+
+def test_workspace_sizes_are_monotone():
+    for dtype in (0, 1):
+        prev = 0
+        for T in (1, 100, 4096, 65536, 184320):
+            s = ext.attn_workspace_size(dtype, 4, T, 32, 8, 128)
+            assert s >= prev and s % 256 == 0
+            prev = s
+    prev = 0
+    for T in (0, 1, 8192, 32768):
+        s = ext.route_workspace_size(1, T, 4096)
+        assert s >= prev
+        prev = s
+    assert ext.attn_workspace_size(0, 1, 100, 6, 4, 128) == 0  # heads not divisible
+
+
+@pytest.mark.parametrize("sparse", [
+    {"kind": "streaming", "sink": 4, "window": 64},
+    {"kind": "streaming", "sink": 0, "window": 1},
+    {"kind": "streaming", "sink": 128, "window": 1024},
+    {"kind": "block", "block": 64, "sink_blocks": 1, "local_blocks": 2, "stride_blocks": 5},
+    {"kind": "block", "block": 128, "sink_blocks": 1, "local_blocks": 8, "stride_blocks": 16},
+    {"kind": "block", "block": 64, "sink_blocks": 0, "local_blocks": 0, "stride_blocks": 0},
+    {"kind": "block", "block": 64, "sink_blocks": 3, "local_blocks": 1, "stride_blocks": 2},
+])
+def test_entry_counter_matches_oracle_enumeration(sparse):
+    lens = [1, 63, 64, 65, 700, 2500]
+    mask = np.array([[1, 0, 0], [0, 1, 0], [0, 0, 1], [1, 1, 0], [0, 1, 1], [1, 0, 1]])
+    got = ext.attn_entries(lens, mask, 6, 3, sparse)
+    assert got == oracle.entries(lens, mask, sparse, 6, 3)
+    assert ext.attn_entries(lens, None, 6, 3, sparse) == oracle.entries(lens, None, sparse, 6, 3)
+
+
+def test_entry_counter_at_workload_sizes():
+    w = syn.WORKLOADS["llama8b-32k-block-router"]
+    assert ext.attn_entries([32768], [[0]], 1, 1, w.sparse) == 68370432
+    assert ext.attn_entries([32768], [[1]], 1, 1, w.sparse) == 32768 * 32769 // 2
+    w = syn.WORKLOADS["qwen-64k-stream-sweep"]
+    assert ext.attn_entries([65536], [[0]], 1, 1, w.sparse) == 140239936
+    w = syn.WORKLOADS["fp32-512-s4w64"]
+    assert ext.attn_entries([512], [[1, 0]], 8, 2, w.sparse) == 4 * (512 * 513 // 2) + 4 * 32538

@@ -30,7 +30,10 @@ def _rand(seed, shape, scale=1.0):
 # --------------------------------------------------------------------------- hand-worked examples
 def test_router_hand_example():
     g = json.load(open(os.path.join(GOLDEN, "hand_examples.json")))["router"]
-    r = oracle.route(np.array(g["hidden"]), [0, 2], np.array(g["w1"]), np.array(g["w2"]), g["threshold"])
+    for exact in (False, True):
+        r = oracle.route(np.array(g["hidden"]), [0, 2], np.array(g["w1"]), np.array(g["w2"]),
+                         g["threshold"], exact=exact)
+        np.testing.assert_array_equal(r["mask"][0], g["mask"])
     np.testing.assert_array_equal(r["pooled"][0], g["pooled"])
     np.testing.assert_array_equal(r["z"][0], g["z"])
     np.testing.assert_array_equal(r["logits"][0], g["logits"])
@@ -241,9 +244,9 @@ def test_router_properties():
     n, d, dr, H = 64, 32, 8, 4
     x = _rand(18, (n, d))
     w1, w2 = _rand(19, (dr, d)), _rand(20, (H, dr))
-    r = oracle.route(x, [0, n], w1, w2, 0.0)
+    r = oracle.route(x, [0, n], w1, w2, 0.0, exact=True)
     perm = np.random.default_rng(21).permutation(n)
-    rp = oracle.route(x[perm], [0, n], w1, w2, 0.0)
+    rp = oracle.route(x[perm], [0, n], w1, w2, 0.0, exact=True)
     np.testing.assert_array_equal(r["pooled"], rp["pooled"])  # exact sums are order-free
     np.testing.assert_array_equal(r["logits"], rp["logits"])
     r4 = oracle.route(4.0 * x, [0, n], w1, w2, 0.0)  # positive homogeneity (ReLU, no bias)
@@ -252,8 +255,9 @@ def test_router_properties():
     rz = oracle.route(np.zeros((n, d)), [0, n], w1, w2, 0.0)
     np.testing.assert_array_equal(rz["logits"], 0.0)
     np.testing.assert_array_equal(rz["mask"], 0)  # ties go to sparse
-    plain = x.sum(0) / n
-    np.testing.assert_allclose(r["pooled"][0], plain, rtol=1e-13, atol=1e-15)
+    plain = oracle.route(x, [0, n], w1, w2, 0.0)  # fp64 sums agree with the exact ones
+    np.testing.assert_allclose(plain["pooled"][0], r["pooled"][0], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(plain["logits"], r["logits"], rtol=1e-12, atol=1e-15)
     assert 0 < r["mask"].sum() < H  # the case is not degenerate
     # the logit is the log-odds of FULL: [l > 0] == [sigmoid(l / T) > 0.5] for any temperature
     for T in (0.1, 1.0, 10.0):

@@ -1,0 +1,59 @@
+// Host-side exhaustive check of the key-tile schedule used by the scheduler and the attention
+// kernels: every (query, key) pair a work item may attend lies in a visited tile, tiles are
+// visited in increasing order, the visit count matches count(), and a tile reported as
+// mask-free holds only visible pairs.
+#include <cstdio>
+#include <vector>
+
+#include "../hybrid_sparse_full_elastic_amd/csrc/elastic_internal.hpp"
+
+using namespace elastic;
+
+static int failures = 0;
+static void fail(const char* what, int mode, int t0, int t1, int BK, int kt) {
+  if (failures++ < 20) std::printf("FAIL %s mode=%d t0=%d t1=%d BK=%d tile=%d\n", what, mode, t0, t1, BK, kt);
+}
+
+int main() {
+  std::vector<Pattern> pats;
+  const int SW[][2] = {{0, 1}, {4, 64}, {1, 1}, {70, 130}, {128, 1024}, {3, 40}, {0, 4096}, {64, 63}};
+  for (auto& s : SW) pats.push_back(Pattern{ELASTIC_SPARSE_STREAMING, s[0], s[1], 64, 0, 0, 0});
+  const int BL[][4] = {{64, 1, 2, 3}, {128, 1, 8, 16}, {128, 0, 1, 0}, {64, 0, 0, 0}, {64, 3, 1, 2}, {128, 2, 0, 1}};
+  for (auto& b : BL) pats.push_back(Pattern{ELASTIC_SPARSE_BLOCK, 0, 1, b[0], b[1], b[2], b[3]});
+  long checked = 0;
+  for (int BK : {32, 64}) {
+    for (int n : {1, 5, 63, 64, 65, 300, 1000, 1500}) {
+      for (int BT : {1, 7, 32, 36, 64, 256}) {
+        for (size_t pi = 0; pi <= pats.size(); ++pi) {
+          const bool full = pi == pats.size();
+          const Pattern p = full ? pats[0] : pats[pi];
+          const int mode = full ? MODE_FULL : p.kind;
+          for (int t0 = 0; t0 < n; t0 += BT) {
+            const int t1 = (t0 + BT < n ? t0 + BT : n) - 1;
+            KeyTiles kt(mode, p, t0, t1, BK);
+            std::vector<char> vis((n + BK - 1) / BK + 2, 0);
+            int prev = -1, cnt = 0;
+            for (int t = kt.next(0); t >= 0; t = kt.next(t + 1)) {
+              if (t <= prev) fail("order", mode, t0, t1, BK, t);
+              if (t >= (int)vis.size()) { fail("range", mode, t0, t1, BK, t); break; }
+              vis[t] = 1; prev = t; ++cnt;
+              if (!kt.needs_mask(t)) {
+                for (int i = t0; i <= t1; ++i)
+                  for (int j = t * BK; j < t * BK + BK; ++j)
+                    if (j >= n || !key_allowed(mode, p, i, j)) { fail("maskfree", mode, t0, t1, BK, t); i = t1 + 1; break; }
+              }
+            }
+            if (cnt != kt.count()) fail("count", mode, t0, t1, BK, cnt);
+            for (int i = t0; i <= t1; ++i)
+              for (int j = 0; j <= i; ++j)
+                if (key_allowed(mode, p, i, j) && !vis[j / BK]) { fail("missed", mode, t0, t1, BK, j / BK); i = t1 + 1; break; }
+            if (!vis[t0 / BK]) fail("diag", mode, t0, t1, BK, t0 / BK);
+            ++checked;
+          }
+        }
+      }
+    }
+  }
+  std::printf("%ld items checked, %d failures\n", checked, failures);
+  return failures ? 1 : 0;
+}
