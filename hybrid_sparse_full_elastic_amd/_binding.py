@@ -7,7 +7,9 @@ from typing import Optional
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libelastic.so")
+# ELASTIC_LIB selects another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("ELASTIC_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                         "libelastic.so")
 ABI_VERSION = 1
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4

@@ -9,7 +9,9 @@
 // Design for CDNA4:
 //  * One workgroup = one work item: a query tile of BT tokens times all G query heads of one
 //    KV head (rows r = token * G + head, so the K/V tile staged in LDS serves the whole GQA
-//    group), 4 waves, each wave owning 2 blocks of 32 query rows.
+//    group), NW waves each owning NB blocks of 32 query rows.  The shipped configuration is
+//    8 waves x 1 block (256 rows): every wave fits in 256 VGPRs, so two waves share a SIMD and
+//    one wave's MFMAs overlap the other's softmax.
 //  * S^T = K . Q^T with v_mfma_f32_32x32x16_bf16: every lane holds one query column, so the
 //    softmax row statistics are per-lane; only one cross-half swap (v_permlane32_swap) per
 //    tile is needed for the maximum.  Q stays in registers for the whole item.
@@ -20,8 +22,11 @@
 //    multiply; fp32 accumulation throughout; masks are evaluated only on tiles that cross a
 //    causal, sink, window or block boundary, and tiles no query of the item may see are
 //    never loaded (streaming items cost O(sink + window), not O(n)).
-//  * K/V tiles are double-buffered in LDS; the next tile's global loads are in flight while
-//    the current tile is multiplied.
+//  * Software pipeline per tile j: Q.K^T of tile j+1 is issued while exp2 of tile j runs,
+//    and P.V of tile j while tile j+1 is masked and reduced to its maximum.  The running
+//    maximum is raised lazily (only when a tile exceeds it by 2^8), so O is almost never
+//    rescaled.  K is staged two tiles ahead and V one tile ahead in double-buffered LDS
+//    slots; global loads run one more tile ahead in registers; one barrier per tile.
 #include "elastic_internal.hpp"
 
 namespace elastic {
@@ -45,22 +50,25 @@ __device__ inline float half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D>
-__global__ __launch_bounds__(BF16_NW * 64, 1) void attn_bf16_kernel(
+template <int D, int NW, int NB>
+__global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens,
     int64_t total_tokens, int Hq, int Hkv, int G, int BT, float scale_log2,
     const int32_t* __restrict__ head_mask, Pattern pat, const WorkItem* __restrict__ items,
     const int32_t* __restrict__ n_items) {
-  constexpr int NW = BF16_NW, NB = BF16_NB, BK = BF16_BK, NT = NW * 64;
+  constexpr int BK = BF16_BK, NT = NW * 64;
   constexpr int DC = D / 16;   // 16-wide d chunks of Q.K^T
   constexpr int DB = D / 32;   // 32-row d blocks of O^T
   constexpr int KST = D + 8;   // K tile row stride in LDS (elements), breaks bank conflicts
   constexpr int VST = BK + 4;  // V^T tile row stride in LDS (elements)
-  constexpr int KCH = BK * D / 8 / NT;                  // 16-byte K chunks per thread
+  constexpr int KCH = (BK * D / 8 + NT - 1) / NT;       // 16-byte K chunks per thread
   constexpr int VUNITS = (BK / 4) * (D / 8);            // (4 keys x 8 d) V units per tile
   constexpr int VPT = (VUNITS + NT - 1) / NT;           // V units per thread
-  static_assert(KCH * NT * 8 == BK * D, "K tile split");
+  // Lazy rescaling: the running maximum is only raised when a tile's maximum exceeds it by
+  // more than 2^SLACK, so p = exp2(s - m) stays <= 2^SLACK and O is rarely rescaled.
+  constexpr float SLACK = 8.0f;
+  static_assert((BK * D / 8) % NT == 0 || NT > BK * D / 8, "K tile split");
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BK * KST];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][D * VST];
@@ -75,12 +83,14 @@ __global__ __launch_bounds__(BF16_NW * 64, 1) void attn_bf16_kernel(
   const bool full = head_mask == nullptr || head_mask[it.seq * Hkv + g] != 0;
   const int mode = full ? MODE_FULL : pat.kind;
   const KeyTiles tiles(mode, pat, t0, t1, BK);
+  const int blk_shift = 31 - __clz(pat.block);  // block sizes are powers of two
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
   const int64_t kv_row = (int64_t)Hkv * D;  // elements between consecutive tokens of k / v
   const uint16_t* kbase = k + seq0 * kv_row + (int64_t)g * D;
   const uint16_t* vbase = v + seq0 * kv_row + (int64_t)g * D;
+  const float c = scale_log2;
 
   // ---- this lane's query rows: r = token * G + head inside the item
   int qi[NB], qhead[NB];
@@ -108,15 +118,18 @@ __global__ __launch_bounds__(BF16_NW * 64, 1) void attn_bf16_kernel(
   // ---- K/V tile staging (global -> registers -> LDS; V transposed to V^T)
   u32x4 kreg[KCH];
   u32x4 vreg[VPT][4];
-  auto load_tile = [&](int kt) {
+  auto load_k = [&](int kt) {
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int idx = tid + c * NT;
+    for (int cc = 0; cc < KCH; ++cc) {
+      const int idx = tid + cc * NT;
       const int row = idx / (D / 8), col8 = idx % (D / 8);
       const int key = kt * BK + row;
-      kreg[c] = key < n ? *reinterpret_cast<const u32x4*>(kbase + key * kv_row + col8 * 8)
-                        : u32x4{0, 0, 0, 0};
+      kreg[cc] = (idx < BK * D / 8 && key < n)
+                     ? *reinterpret_cast<const u32x4*>(kbase + key * kv_row + col8 * 8)
+                     : u32x4{0, 0, 0, 0};
     }
+  };
+  auto load_v = [&](int kt) {
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
       const int idx = tid + u * NT;
@@ -130,13 +143,15 @@ __global__ __launch_bounds__(BF16_NW * 64, 1) void attn_bf16_kernel(
       }
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_k = [&](int buf) {
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int idx = tid + c * NT;
+    for (int cc = 0; cc < KCH; ++cc) {
+      const int idx = tid + cc * NT;
       const int row = idx / (D / 8), col8 = idx % (D / 8);
-      *reinterpret_cast<u32x4*>(&k_lds[buf][row * KST + col8 * 8]) = kreg[c];
+      if (idx < BK * D / 8) *reinterpret_cast<u32x4*>(&k_lds[buf][row * KST + col8 * 8]) = kreg[cc];
     }
+  };
+  auto store_v = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
       const int idx = tid + u * NT;
@@ -154,39 +169,10 @@ __global__ __launch_bounds__(BF16_NW * 64, 1) void attn_bf16_kernel(
     }
   };
 
-  // ---- running state
-  f32x16 oacc[DB][NB];
-  float m_run[NB], l_run[NB];
-#pragma unroll
-  for (int qb = 0; qb < NB; ++qb) {
-    m_run[qb] = -1.0e30f;  // finite: a fully masked first tile leaves alpha = 1, p = 0
-    l_run[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[db][qb][e] = 0.f;
-  }
-
-  int kt = tiles.next(0);
-  int buf = 0;
-  if (kt >= 0) {
-    load_tile(kt);
-    store_tile(0);
-  }
-  while (kt >= 0) {
-    const int nkt = tiles.next(kt + 1);
-    if (nkt >= 0) load_tile(nkt);
-    __syncthreads();
-
-    // S^T[key, query] for two 32-key blocks x NB 32-query blocks
-    f32x16 sacc[2][NB];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < NB; ++qb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[kb][qb][e] = 0.f;
+  // ---- S^T[key, query] = K . Q^T for the two 32-key halves of a tile
+  auto qk = [&](int buf, f32x16 (&s)[2][NB]) {
     const uint16_t* ks = &k_lds[buf][0];
+    const f32x16 zero = {};
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
       bf16x8 a[2];
@@ -197,67 +183,190 @@ __global__ __launch_bounds__(BF16_NW * 64, 1) void attn_bf16_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int qb = 0; qb < NB; ++qb)
-          sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], qreg[qb][dc], sacc[kb][qb], 0, 0, 0);
+          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], qreg[qb][dc],
+                                                             dc == 0 ? zero : s[kb][qb], 0, 0, 0);
     }
+  };
 
-    // online softmax (exp2 domain); P^T packed to bf16 in MFMA B-operand order
-    const bool masked = tiles.needs_mask(kt);
-    bf16x8 pop[2][2][NB];
+  // ---- masks: allowed(j) = j <= hi && (j < a || j >= b), exact per (query, key)
+  int qblk[NB];
+#pragma unroll
+  for (int qb = 0; qb < NB; ++qb) qblk[qb] = qi[qb] >> blk_shift;
+  auto apply_mask = [&](f32x16 (&s)[2][NB], int kt) {
+    const int kblk = (kt * BK) >> blk_shift;  // one key block per tile (block % BK == 0)
+    const bool kvis_static = kblk < pat.sink_blocks ||
+                             (pat.stride_blocks > 0 && kblk % pat.stride_blocks == 0);
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb) {
-      float mt = -__builtin_huge_valf();
+      const int i = qi[qb];
+      const int hi = qvalid[qb] ? i : -1;
+      int a = 0, b = 0;
+      if (mode == MODE_STREAM) {
+        a = pat.sink;
+        b = i - pat.window + 1;
+      } else if (mode == MODE_BLOCK) {
+        b = (kvis_static || qblk[qb] - kblk <= pat.local_blocks) ? 0 : 0x7fffffff;
+      }
+      const int base = kt * BK + half * 4;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          float x = sacc[kb][qb][e] * scale_log2;
-          if (masked) {
-            const int j = kt * BK + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-            if (!qvalid[qb] || !key_allowed(mode, pat, qi[qb], j)) x = -__builtin_huge_valf();
-          }
-          sacc[kb][qb][e] = x;
-          mt = fmaxf(mt, x);
+          const int j = base + kb * 32 + (e >> 2) * 8 + (e & 3);
+          const bool ok = j <= hi && (j < a || j >= b);
+          if (!ok) s[kb][qb][e] = -__builtin_huge_valf();
         }
-      mt = half_max(mt);
-      const float m_new = fmaxf(m_run[qb], mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-      m_run[qb] = m_new;
-      float ls = 0.f;
+    }
+  };
+  auto tile_max = [&](f32x16 (&s)[2][NB], float (&mt)[NB]) {
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb) {
+      float m0 = fmaxf(s[0][qb][0], s[1][qb][0]), m1 = fmaxf(s[0][qb][1], s[1][qb][1]);
+#pragma unroll
+      for (int e = 2; e < 16; e += 2) {
+        m0 = fmaxf(m0, fmaxf(s[0][qb][e], s[1][qb][e]));
+        m1 = fmaxf(m1, fmaxf(s[0][qb][e + 1], s[1][qb][e + 1]));
+      }
+      mt[qb] = half_max(fmaxf(m0, m1));
+    }
+  };
+
+  // ---- running state (m in the scaled log2 domain)
+  f32x16 oacc[DB][NB];
+  float m_sc[NB], l_run[NB], alpha[NB];
+#pragma unroll
+  for (int qb = 0; qb < NB; ++qb) {
+    m_sc[qb] = -1.0e30f;  // finite: fully masked tiles give p = 0 and never raise it
+    l_run[qb] = 0.f;
+    alpha[qb] = 1.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[db][qb][e] = 0.f;
+  }
+  bool pending = false;  // wave-uniform: O and l wait for a multiply by alpha
+
+  // Raise the running maximum for the scores in s (raw, masked); decide the rescale.
+  auto update_max = [&](f32x16 (&s)[2][NB]) {
+    float mt[NB];
+    tile_max(s, mt);
+    bool need = false;
+    float mn[NB];
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb) {
+      const float ms = mt[qb] * c;
+      need |= ms > m_sc[qb] + SLACK;
+      mn[qb] = fmaxf(m_sc[qb], ms);
+    }
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+      for (int qb = 0; qb < NB; ++qb) {
+        alpha[qb] = __builtin_amdgcn_exp2f(m_sc[qb] - mn[qb]);
+        m_sc[qb] = mn[qb];
+      }
+      pending = true;
+    }
+  };
+
+  // ---- tile schedule: kt_cur = tile j, kt_n1 = j+1, kt_n2 = j+2
+  int kt_cur = tiles.next(0);
+  if (kt_cur < 0) return;  // cannot happen: the diagonal tile is always visited
+  int kt_n1 = tiles.next(kt_cur + 1);
+  int kt_n2 = kt_n1 >= 0 ? tiles.next(kt_n1 + 1) : -1;
+
+  // prologue: tile 0 (K and V) and K of tile 1 into LDS; registers hold K_2 and V_1
+  load_k(kt_cur);
+  load_v(kt_cur);
+  store_k(0);
+  store_v(0);
+  if (kt_n1 >= 0) {
+    load_k(kt_n1);
+    load_v(kt_n1);
+    store_k(1);
+  }
+  if (kt_n2 >= 0) load_k(kt_n2);
+  __syncthreads();
+  f32x16 s0[2][NB], s1[2][NB];
+  qk(0, s0);
+  __syncthreads();  // every wave is done with K slot 0 before it is refilled
+  if (tiles.needs_mask(kt_cur)) apply_mask(s0, kt_cur);
+  update_max(s0);
+  pending = false;  // O and l are still zero
+  int slot = 0;
+
+  // One pipelined step on tile j: Q.K^T of tile j+1 and exp of tile j, then P.V of tile j
+  // and the mask / maximum of tile j+1; LDS refills of K_{j+2} and V_{j+1}; global loads of
+  // K_{j+3} and V_{j+2}; one barrier.
+  auto step = [&](f32x16 (&sc)[2][NB], f32x16 (&sn)[2][NB]) {
+    if (pending) {
+#pragma unroll
+      for (int qb = 0; qb < NB; ++qb) {
+        l_run[qb] *= alpha[qb];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[db][qb][e] *= alpha[qb];
+      }
+      pending = false;
+    }
+    const bool has_next = kt_n1 >= 0;
+    // phase A: S_{j+1} (MFMA) while p_j = exp2(c s_j - m) (VALU)
+    qk(slot ^ 1, sn);
+    bf16x8 pop[2][2][NB];
+    float lsum4[NB][4];
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb) {
+      lsum4[qb][0] = lsum4[qb][1] = lsum4[qb][2] = lsum4[qb][3] = 0.f;
+      const float nm = -m_sc[qb];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = __builtin_amdgcn_exp2f(sacc[kb][qb][e] - m_new);
-          ls += p;
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][qb][e], c, nm));
+          lsum4[qb][e & 3] += p;
           pop[kb][e >> 3][qb][e & 7] = (__bf16)p;
         }
-      l_run[qb] = l_run[qb] * alpha + ls;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[db][qb][e] *= alpha;
     }
-
-    // O^T[d, query] += V^T[d, key] . P^T[key, query]
-    const uint16_t* vs = &v_lds[buf][0];
+    // phase B: O^T += V^T P^T (MFMA) while l += sum p and the next tile's max (VALU)
+    const uint16_t* vs = &v_lds[slot][0];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const uint16_t* row = vs + (db * 32 + l32) * VST + kb * 32 + c * 16 + half * 4;
+        for (int cc = 0; cc < 2; ++cc) {
+          const uint16_t* row = vs + (db * 32 + l32) * VST + kb * 32 + cc * 16 + half * 4;
           const u32x2 lo = *reinterpret_cast<const u32x2*>(row);
           const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 8);
           const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
           for (int qb = 0; qb < NB; ++qb)
-            oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[kb][c][qb], oacc[db][qb], 0, 0, 0);
+            oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[kb][cc][qb], oacc[db][qb], 0, 0, 0);
         }
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb)
+      l_run[qb] += (lsum4[qb][0] + lsum4[qb][1]) + (lsum4[qb][2] + lsum4[qb][3]);
+    if (has_next) {
+      if (tiles.needs_mask(kt_n1)) apply_mask(sn, kt_n1);
+      update_max(sn);
+    }
+    if (kt_n2 >= 0) store_k(slot);
+    if (has_next) store_v(slot ^ 1);
+    const int kt_n3 = kt_n2 >= 0 ? tiles.next(kt_n2 + 1) : -1;
+    if (kt_n3 >= 0) load_k(kt_n3);
+    if (kt_n2 >= 0) load_v(kt_n2);
+    __syncthreads();
+    kt_cur = kt_n1;
+    kt_n1 = kt_n2;
+    kt_n2 = kt_n3;
+    slot ^= 1;
+  };
 
-    if (nkt >= 0) store_tile(buf ^ 1);
-    buf ^= 1;
-    kt = nkt;
+  while (true) {
+    step(s0, s1);
+    if (kt_cur < 0) break;
+    step(s1, s0);
+    if (kt_cur < 0) break;
   }
 
   // ---- epilogue: normalise, store bf16 O (and the natural-log LSE)
@@ -277,11 +386,23 @@ __global__ __launch_bounds__(BF16_NW * 64, 1) void attn_bf16_kernel(
         *reinterpret_cast<u32x2*>(dst + db * 32 + ig * 8 + half * 4) = __builtin_bit_cast(u32x2, w);
       }
     if (lse != nullptr && half == 0)
-      lse[(int64_t)qhead[qb] * total_tokens + seq0 + qi[qb]] = (m_run[qb] + __log2f(lt)) * LN2;
+      lse[(int64_t)qhead[qb] * total_tokens + seq0 + qi[qb]] = (m_sc[qb] + __log2f(lt)) * LN2;
   }
 }
 
 }  // namespace
+
+template <int D, int NW, int NB>
+static void launch_cfg(int64_t grid, hipStream_t stream, const void* q, const void* k, const void* v,
+                       void* o, float* lse, const int32_t* cu_seqlens, int64_t total_tokens,
+                       int n_q_heads, int n_kv_heads, int G, int BT, float scale_log2,
+                       const int32_t* head_mask, const Pattern& pat, const WorkItem* items,
+                       const int32_t* n_items) {
+  hipLaunchKernelGGL((attn_bf16_kernel<D, NW, NB>), dim3((unsigned)grid), dim3(NW * 64), 0, stream,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
+                     cu_seqlens, total_tokens, n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask,
+                     pat, items, n_items);
+}
 
 hipError_t launch_attn_bf16(int head_dim, const void* q, const void* k, const void* v, void* o,
                             float* lse, const int32_t* cu_seqlens, int64_t total_tokens,
@@ -290,19 +411,15 @@ hipError_t launch_attn_bf16(int head_dim, const void* q, const void* k, const vo
                             const int32_t* n_items, int64_t grid, hipStream_t stream) {
   const float scale_log2 = scale * 1.4426950408889634f;
   const int G = n_q_heads / n_kv_heads;
-  const dim3 block(BF16_NW * 64);
   if (grid <= 0) return hipSuccess;
-  if (head_dim == 128) {
-    hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3((unsigned)grid), block, 0, stream,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
-                       cu_seqlens, total_tokens, n_q_heads, n_kv_heads, G, BT, scale_log2,
-                       head_mask, pat, items, n_items);
-  } else {
-    hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3((unsigned)grid), block, 0, stream,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
-                       cu_seqlens, total_tokens, n_q_heads, n_kv_heads, G, BT, scale_log2,
-                       head_mask, pat, items, n_items);
-  }
+  if (head_dim == 128)
+    launch_cfg<128, BF16_NW, BF16_NB>(grid, stream, q, k, v, o, lse, cu_seqlens, total_tokens,
+                                      n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask, pat,
+                                      items, n_items);
+  else
+    launch_cfg<64, BF16_NW, BF16_NB>(grid, stream, q, k, v, o, lse, cu_seqlens, total_tokens,
+                                     n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask, pat,
+                                     items, n_items);
   return hipGetLastError();
 }
 

@@ -112,8 +112,8 @@ struct KeyTiles {
 
 // ------------------------------------------------------------------ tile configurations
 // bf16 MFMA attention: NW waves x NB blocks of 32 query rows per workgroup, 64-key tiles.
-constexpr int BF16_NW = 4;
-constexpr int BF16_NB = 2;
+constexpr int BF16_NW = 8;
+constexpr int BF16_NB = 1;
 constexpr int BF16_ROWS = BF16_NW * BF16_NB * 32;  // query rows (token, head) per workgroup
 constexpr int BF16_BK = 64;
 // fp32 attention: one thread per query row, 32-key tiles.
