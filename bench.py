@@ -34,6 +34,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
     p.add_argument("--no-supplements", action="store_true")
     p.add_argument("--scaling", action="store_true", help="streaming-window and length scaling sweep")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="run one plain 1 GiB device-to-device copy first (calibrates HBM byte counters)")
     return p.parse_args()
 
 
@@ -97,6 +99,14 @@ def main():
                          sparse=w.sparse, out=o, workspace=ws_attn)
         if ev is not None:
             ev[2].record(stream)
+
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

@@ -37,6 +37,9 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr float LN2 = 0.69314718055994530942f;
 
@@ -50,39 +53,50 @@ __device__ inline float half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, int NW, int NB>
-__global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens,
-    int64_t total_tokens, int Hq, int Hkv, int G, int BT, float scale_log2,
-    const int32_t* __restrict__ head_mask, Pattern pat, const WorkItem* __restrict__ items,
-    const int32_t* __restrict__ n_items) {
+template <int D>
+struct LdsTiles {
+  // Row strides in elements.  K rows: +8 spreads a wave's 16-byte row reads over all banks.
+  // V rows: +32 makes the four key rows of one transposing read start 16 banks apart, so
+  // each half-wave of ds_read_b64_tr_b16 touches every bank exactly once.
+  static constexpr int KST = D + 8;
+  static constexpr int VST = D + 32;
+  uint16_t k[2][BF16_BK * KST];
+  uint16_t v[2][BF16_BK * VST];
+};
+
+// max of three floats in one instruction (the inputs are never NaN here)
+__device__ inline float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// One work item with its mode known at compile time.
+template <int D, int NW, int NB, int MODE>
+__device__ __forceinline__ void attn_item(
+    const WorkItem& it, LdsTiles<D>& lds, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
+    float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens, int64_t total_tokens, int Hq,
+    int Hkv, int G, int BT, float scale_log2, const Pattern& pat) {
   constexpr int BK = BF16_BK, NT = NW * 64;
   constexpr int DC = D / 16;   // 16-wide d chunks of Q.K^T
   constexpr int DB = D / 32;   // 32-row d blocks of O^T
-  constexpr int KST = D + 8;   // K tile row stride in LDS (elements), breaks bank conflicts
-  constexpr int VST = BK + 4;  // V^T tile row stride in LDS (elements)
+  constexpr int KST = LdsTiles<D>::KST, VST = LdsTiles<D>::VST;
   constexpr int KCH = (BK * D / 8 + NT - 1) / NT;       // 16-byte K chunks per thread
-  constexpr int VUNITS = (BK / 4) * (D / 8);            // (4 keys x 8 d) V units per tile
-  constexpr int VPT = (VUNITS + NT - 1) / NT;           // V units per thread
   // Lazy rescaling: the running maximum is only raised when a tile's maximum exceeds it by
   // more than 2^SLACK, so p = exp2(s - m) stays <= 2^SLACK and O is rarely rescaled.
   constexpr float SLACK = 8.0f;
   static_assert((BK * D / 8) % NT == 0 || NT > BK * D / 8, "K tile split");
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BK * KST];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][D * VST];
-
-  if ((int)blockIdx.x >= *n_items) return;
-  const WorkItem it = items[blockIdx.x];
+  auto& k_lds = lds.k;
+  auto& v_lds = lds.v;
   const int64_t seq0 = cu_seqlens ? cu_seqlens[it.seq] : 0;
   const int n = cu_seqlens ? cu_seqlens[it.seq + 1] - (int)seq0 : (int)total_tokens;
   const int t0 = it.qtile * BT;
   const int t1 = min(t0 + BT, n) - 1;
   const int g = it.group;
-  const bool full = head_mask == nullptr || head_mask[it.seq * Hkv + g] != 0;
-  const int mode = full ? MODE_FULL : pat.kind;
-  const KeyTiles tiles(mode, pat, t0, t1, BK);
+  constexpr int mode = MODE;
+  const KeyTilesT<MODE> tiles(MODE, pat, t0, t1, BK);
   const int blk_shift = 31 - __clz(pat.block);  // block sizes are powers of two
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -91,6 +105,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(
   const uint16_t* kbase = k + seq0 * kv_row + (int64_t)g * D;
   const uint16_t* vbase = v + seq0 * kv_row + (int64_t)g * D;
   const float c = scale_log2;
+  // source address of this lane in a transposing V read: key (l/4) + 4*half of the 16-key
+  // chunk, columns (group parity)*16 + 4*(l%4) of the 32-column d block
+  const int v_lane_off = ((lane & 15) / 4 + 4 * half) * VST + ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
 
   // ---- this lane's query rows: r = token * G + head inside the item
   int qi[NB], qhead[NB];
@@ -115,59 +132,40 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(
     }
   }
 
-  // ---- K/V tile staging (global -> registers -> LDS; V transposed to V^T)
+  // ---- K/V tile staging: global -> registers -> LDS, both row-major [key][d]
   u32x4 kreg[KCH];
-  u32x4 vreg[VPT][4];
-  auto load_k = [&](int kt) {
+  u32x4 vreg[KCH];
+  // Raw buffer loads: a per-tile descriptor covers only the tile's rows that exist in the
+  // sequence, so rows past its end read as zero without branches.
+  auto tile_rsrc = [&](const uint16_t* base, int kt) {
+    const int rows = min(n - kt * BK, BK);
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(base + (int64_t)kt * BK * kv_row), (short)0,
+        rows * (int)kv_row * 2, 0x00020000);
+  };
+  auto load_tile = [&](const uint16_t* base, int kt, u32x4 (&reg)[KCH]) {
+    const auto rs = tile_rsrc(base, kt);
 #pragma unroll
     for (int cc = 0; cc < KCH; ++cc) {
       const int idx = tid + cc * NT;
       const int row = idx / (D / 8), col8 = idx % (D / 8);
-      const int key = kt * BK + row;
-      kreg[cc] = (idx < BK * D / 8 && key < n)
-                     ? *reinterpret_cast<const u32x4*>(kbase + key * kv_row + col8 * 8)
-                     : u32x4{0, 0, 0, 0};
+      if (idx < BK * D / 8)
+        reg[cc] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (row * (int)kv_row + col8 * 8) * 2, 0, 0));
     }
   };
-  auto load_v = [&](int kt) {
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int idx = tid + u * NT;
-      const int kq = idx / (D / 8), d8 = idx % (D / 8);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kt * BK + kq * 4 + r;
-        vreg[u][r] = (idx < VUNITS && key < n)
-                         ? *reinterpret_cast<const u32x4*>(vbase + key * kv_row + d8 * 8)
-                         : u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_k = [&](int buf) {
+  auto load_k = [&](int kt) { load_tile(kbase, kt, kreg); };
+  auto load_v = [&](int kt) { load_tile(vbase, kt, vreg); };
+  auto store_tile = [&](uint16_t* dst, int stride, const u32x4 (&reg)[KCH]) {
 #pragma unroll
     for (int cc = 0; cc < KCH; ++cc) {
       const int idx = tid + cc * NT;
       const int row = idx / (D / 8), col8 = idx % (D / 8);
-      if (idx < BK * D / 8) *reinterpret_cast<u32x4*>(&k_lds[buf][row * KST + col8 * 8]) = kreg[cc];
+      if (idx < BK * D / 8) *reinterpret_cast<u32x4*>(dst + row * stride + col8 * 8) = reg[cc];
     }
   };
-  auto store_v = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int idx = tid + u * NT;
-      if (idx < VUNITS) {
-        const int kq = idx / (D / 8), d8 = idx % (D / 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int w = e >> 1, sh = (e & 1) * 16;
-          const uint32_t x0 = (vreg[u][0][w] >> sh) & 0xffffu, x1 = (vreg[u][1][w] >> sh) & 0xffffu;
-          const uint32_t x2 = (vreg[u][2][w] >> sh) & 0xffffu, x3 = (vreg[u][3][w] >> sh) & 0xffffu;
-          *reinterpret_cast<u32x2*>(&v_lds[buf][(d8 * 8 + e) * VST + kq * 4]) =
-              u32x2{x0 | (x1 << 16), x2 | (x3 << 16)};
-        }
-      }
-    }
-  };
+  auto store_k = [&](int buf) { store_tile(&k_lds[buf][0], KST, kreg); };
+  auto store_v = [&](int buf) { store_tile(&v_lds[buf][0], VST, vreg); };
 
   // ---- S^T[key, query] = K . Q^T for the two 32-key halves of a tile
   auto qk = [&](int buf, f32x16 (&s)[2][NB]) {
@@ -221,13 +219,14 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(
   auto tile_max = [&](f32x16 (&s)[2][NB], float (&mt)[NB]) {
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb) {
-      float m0 = fmaxf(s[0][qb][0], s[1][qb][0]), m1 = fmaxf(s[0][qb][1], s[1][qb][1]);
+      float m0 = max3f(s[0][qb][0], s[1][qb][0], s[0][qb][1]);
+      float m1 = max3f(s[1][qb][1], s[0][qb][2], s[1][qb][2]);
 #pragma unroll
-      for (int e = 2; e < 16; e += 2) {
-        m0 = fmaxf(m0, fmaxf(s[0][qb][e], s[1][qb][e]));
-        m1 = fmaxf(m1, fmaxf(s[0][qb][e + 1], s[1][qb][e + 1]));
+      for (int e = 3; e < 15; e += 2) {
+        m0 = max3f(m0, s[0][qb][e], s[1][qb][e]);
+        m1 = max3f(m1, s[0][qb][e + 1], s[1][qb][e + 1]);
       }
-      mt[qb] = half_max(fmaxf(m0, m1));
+      mt[qb] = half_max(max3f(m0, m1, max3f(s[0][qb][15], s[1][qb][15], m0)));
     }
   };
 
@@ -328,17 +327,21 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(
         }
     }
     // phase B: O^T += V^T P^T (MFMA) while l += sum p and the next tile's max (VALU)
-    const uint16_t* vs = &v_lds[slot][0];
+    // V^T A-operands straight from the row-major V tile: ds_read_b64_tr_b16 hands lane
+    // (16-lane group gr, index l) V[key_i][dbase + l] for the four keys key_i its group's
+    // source lanes point at; two reads give the 8 key slots of the MFMA lane.
+    const uint16_t* vs = &v_lds[slot][0] + v_lane_off;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-          const uint16_t* row = vs + (db * 32 + l32) * VST + kb * 32 + cc * 16 + half * 4;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(row);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 8);
-          const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+          const uint16_t* src = vs + (kb * 32 + cc * 16) * VST + db * 32;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 8 * VST));
+          const bf16x8 a = __builtin_bit_cast(
+              bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 #pragma unroll
           for (int qb = 0; qb < NB; ++qb)
             oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[kb][cc][qb], oacc[db][qb], 0, 0, 0);
@@ -388,6 +391,28 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(
     if (lse != nullptr && half == 0)
       lse[(int64_t)qhead[qb] * total_tokens + seq0 + qi[qb]] = (m_sc[qb] + __log2f(lt)) * LN2;
   }
+}
+
+template <int D, int NW, int NB>
+__global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens,
+    int64_t total_tokens, int Hq, int Hkv, int G, int BT, float scale_log2,
+    const int32_t* __restrict__ head_mask, Pattern pat, const WorkItem* __restrict__ items,
+    const int32_t* __restrict__ n_items) {
+  __shared__ __attribute__((aligned(16))) LdsTiles<D> lds;
+  if ((int)blockIdx.x >= *n_items) return;
+  const WorkItem it = items[blockIdx.x];
+  const bool full = head_mask == nullptr || head_mask[it.seq * Hkv + it.group] != 0;
+  if (full)
+    attn_item<D, NW, NB, MODE_FULL>(it, lds, q, k, v, o, lse, cu_seqlens, total_tokens, Hq, Hkv, G,
+                                    BT, scale_log2, pat);
+  else if (pat.kind == ELASTIC_SPARSE_STREAMING)
+    attn_item<D, NW, NB, MODE_STREAM>(it, lds, q, k, v, o, lse, cu_seqlens, total_tokens, Hq, Hkv,
+                                      G, BT, scale_log2, pat);
+  else
+    attn_item<D, NW, NB, MODE_BLOCK>(it, lds, q, k, v, o, lse, cu_seqlens, total_tokens, Hq, Hkv,
+                                     G, BT, scale_log2, pat);
 }
 
 }  // namespace

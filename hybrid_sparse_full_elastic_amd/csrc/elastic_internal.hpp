@@ -42,25 +42,29 @@ __host__ __device__ inline bool key_allowed(int mode, const Pattern& p, int i, i
          (p.stride_blocks > 0 && kb % p.stride_blocks == 0);
 }
 
-// Key tiles visited by the query tokens [t0, t1] (inclusive) of one work item.
-struct KeyTiles {
-  int mode, BK, t0, t1, last;
+// Key tiles visited by the query tokens [t0, t1] (inclusive) of one work item.  M is the
+// mode when it is known at compile time (MODE_*), or -1 to take it from the constructor.
+template <int M = -1>
+struct KeyTilesT {
+  int mode_rt, BK, t0, t1, last;
   Pattern p;
   int sink_end, win_begin;  // streaming: tiles [0, sink_end) and [win_begin, last]
   int tpb, qb0, qb1;        // block: tiles per block, query blocks of t0 and t1
 
-  __host__ __device__ KeyTiles(int mode_, const Pattern& p_, int t0_, int t1_, int BK_)
-      : mode(mode_), BK(BK_), t0(t0_), t1(t1_), last(t1_ / BK_), p(p_) {
+  __host__ __device__ int mode() const { return M >= 0 ? M : mode_rt; }
+
+  __host__ __device__ KeyTilesT(int mode_, const Pattern& p_, int t0_, int t1_, int BK_)
+      : mode_rt(mode_), BK(BK_), t0(t0_), t1(t1_), last(t1_ / BK_), p(p_) {
     sink_end = 0;
     win_begin = 0;
     tpb = 1;
     qb0 = qb1 = 0;
-    if (mode == MODE_STREAM) {
+    if (mode() == MODE_STREAM) {
       const int sink_keys = p.sink < t1 + 1 ? p.sink : t1 + 1;
       sink_end = (sink_keys + BK - 1) / BK;
       const int w0 = t0 - p.window + 1;
       win_begin = w0 > 0 ? w0 / BK : 0;
-    } else if (mode == MODE_BLOCK) {
+    } else if (mode() == MODE_BLOCK) {
       tpb = p.block / BK;  // block_size is a multiple of BK (checked on the host)
       qb0 = t0 / p.block;
       qb1 = t1 / p.block;
@@ -81,9 +85,9 @@ struct KeyTiles {
   // Smallest visited tile >= kt, or -1 when there is none.
   __host__ __device__ int next(int kt) const {
     if (kt > last) return -1;
-    if (mode == MODE_STREAM) {
+    if (mode() == MODE_STREAM) {
       if (kt >= sink_end && kt < win_begin) kt = win_begin;
-    } else if (mode == MODE_BLOCK) {
+    } else if (mode() == MODE_BLOCK) {
       const int kb = kt / tpb;
       const int nb = next_block(kb);
       if (nb != kb) kt = nb * tpb;
@@ -95,20 +99,26 @@ struct KeyTiles {
   __host__ __device__ bool needs_mask(int kt) const {
     const int k0 = kt * BK, k1 = k0 + BK - 1;
     if (k1 > t0) return true;  // causal edge (also covers keys past the sequence end)
-    if (mode == MODE_FULL) return false;
-    if (mode == MODE_STREAM) return !(k1 < p.sink || k0 > t1 - p.window);
+    if (mode() == MODE_FULL) return false;
+    if (mode() == MODE_STREAM) return !(k1 < p.sink || k0 > t1 - p.window);
     const int kb = k0 / p.block;
     return !(kb < p.sink_blocks || kb >= qb1 - p.local_blocks ||
              (p.stride_blocks > 0 && kb % p.stride_blocks == 0));
   }
 
   __host__ __device__ int count() const {
-    if (mode == MODE_FULL) return last + 1;
+    if (mode() == MODE_FULL) return last + 1;
+    if (mode() == MODE_STREAM) {  // [0, sink_end) U [win_begin, last], clipped to [0, last]
+      const int se = sink_end < last + 1 ? sink_end : last + 1;
+      const int wb = win_begin > se ? win_begin : se;
+      return se + (last >= wb ? last - wb + 1 : 0);
+    }
     int c = 0;
     for (int kt = next(0); kt >= 0; kt = next(kt + 1)) ++c;
     return c;
   }
 };
+using KeyTiles = KeyTilesT<-1>;
 
 // ------------------------------------------------------------------ tile configurations
 // bf16 MFMA attention: NW waves x NB blocks of 32 query rows per workgroup, 64-key tiles.

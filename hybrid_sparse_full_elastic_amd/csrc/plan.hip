@@ -16,11 +16,9 @@ namespace elastic {
 namespace {
 
 constexpr int PLAN_THREADS = 1024;
-constexpr int PLAN_BUCKETS = 4096;  // costs >= PLAN_BUCKETS - 1 share the last bucket
-
-__device__ inline int seq_len(const int32_t* cu, int b, int64_t total) {
-  return cu ? cu[b + 1] - cu[b] : (int)total;
-}
+constexpr int PLAN_BUCKETS = 4096;   // costs >= PLAN_BUCKETS - 1 share the last bucket
+constexpr int PLAN_LDS_SEQ = 2048;   // sequences whose lengths / tile offsets are cached in LDS
+constexpr int PLAN_LDS_MASK = 16384; // head-mask entries cached in LDS
 
 __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     const int32_t* __restrict__ cu_seqlens, int batch, int64_t total_tokens, int n_kv_heads,
@@ -29,15 +27,33 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
   __shared__ int hist[PLAN_BUCKETS];
   __shared__ int cursor[PLAN_BUCKETS];
   __shared__ int scan_tmp[PLAN_THREADS];
+  __shared__ int s_prefix[PLAN_LDS_SEQ + 1];
+  __shared__ int s_len[PLAN_LDS_SEQ];
+  __shared__ unsigned char s_full[PLAN_LDS_MASK];
   __shared__ int carry;
   const int tid = threadIdx.x;
+  const bool seq_cached = batch <= PLAN_LDS_SEQ;
+  const bool mask_cached = (int64_t)batch * n_kv_heads <= PLAN_LDS_MASK;
 
-  // 1. tile_prefix[b] = query tiles of sequences before b (block-wide scan in chunks).
+  auto seq_len = [&](int b) -> int {
+    return cu_seqlens ? cu_seqlens[b + 1] - cu_seqlens[b] : (int)total_tokens;
+  };
+
+  // 1. tile_prefix[b] = query tiles of the sequences before b (block-wide scan in chunks).
   if (tid == 0) carry = 0;
+  for (int i = tid; i < PLAN_BUCKETS; i += PLAN_THREADS) {
+    hist[i] = 0;
+    cursor[i] = 0;
+  }
+  if (mask_cached) {
+    for (int i = tid; i < batch * n_kv_heads; i += PLAN_THREADS)
+      s_full[i] = head_mask == nullptr || head_mask[i] != 0;
+  }
   __syncthreads();
   for (int base = 0; base < batch; base += PLAN_THREADS) {
     const int b = base + tid;
-    const int nt = b < batch ? (seq_len(cu_seqlens, b, total_tokens) + BT - 1) / BT : 0;
+    const int len = b < batch ? seq_len(b) : 0;
+    const int nt = (len + BT - 1) / BT;
     scan_tmp[tid] = nt;
     __syncthreads();
     for (int off = 1; off < PLAN_THREADS; off <<= 1) {
@@ -46,60 +62,81 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
       scan_tmp[tid] += add;
       __syncthreads();
     }
-    if (b < batch) tile_prefix[b] = carry + scan_tmp[tid] - nt;
+    if (b < batch) {
+      const int pre = carry + scan_tmp[tid] - nt;
+      tile_prefix[b] = pre;
+      if (seq_cached) {
+        s_prefix[b] = pre;
+        s_len[b] = len;
+      }
+    }
     __syncthreads();
     if (tid == PLAN_THREADS - 1) carry += scan_tmp[tid];
     __syncthreads();
   }
   const int total_tiles = carry;
-  if (tid == 0) tile_prefix[batch] = total_tiles;
+  if (tid == 0) {
+    tile_prefix[batch] = total_tiles;
+    if (seq_cached) s_prefix[batch] = total_tiles;
+  }
+  __syncthreads();
   int64_t count = (int64_t)total_tiles * n_kv_heads;
   if (count > max_items) count = max_items;  // cannot happen for consistent cu_seqlens
   const int nitem = (int)count;
 
-  for (int i = tid; i < PLAN_BUCKETS; i += PLAN_THREADS) {
-    hist[i] = 0;
-    cursor[i] = 0;
-  }
-  __syncthreads();
-
-  // 2. Enumerate items u = tile * n_kv_heads + g, cost each and histogram the costs.
+  // 2. Items u = tile * n_kv_heads + g: locate, cost and histogram them.
   auto describe = [&](int u, WorkItem& it) {
     const int tile = u / n_kv_heads;
     const int g = u - tile * n_kv_heads;
-    int lo = 0, hi = batch - 1;  // last b with tile_prefix[b] <= tile
+    int lo = 0, hi = batch - 1;  // last b with prefix[b] <= tile
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (tile_prefix[mid] <= tile) lo = mid; else hi = mid - 1;
+      const int pm = seq_cached ? s_prefix[mid] : tile_prefix[mid];
+      if (pm <= tile) lo = mid; else hi = mid - 1;
     }
     const int b = lo;
-    const int qt = tile - tile_prefix[b];
-    const int n = seq_len(cu_seqlens, b, total_tokens);
+    const int qt = tile - (seq_cached ? s_prefix[b] : tile_prefix[b]);
+    const int n = seq_cached ? s_len[b] : seq_len(b);
     const int t0 = qt * BT;
     const int t1 = min(t0 + BT, n) - 1;
-    const bool full = head_mask == nullptr || head_mask[b * n_kv_heads + g] != 0;
-    KeyTiles kt(full ? MODE_FULL : pat.kind, pat, t0, t1, BK);
+    const int mi = b * n_kv_heads + g;
+    const bool full = mask_cached ? s_full[mi] != 0 : (head_mask == nullptr || head_mask[mi] != 0);
+    const KeyTiles kt(full ? MODE_FULL : pat.kind, pat, t0, t1, BK);
     it.seq = b;
     it.group = g;
     it.qtile = qt;
     it.cost = kt.count();
   };
-  __threadfence_block();
   for (int u = tid; u < nitem; u += PLAN_THREADS) {
     WorkItem it;
     describe(u, it);
-    const int bucket = min(it.cost, PLAN_BUCKETS - 1);
-    atomicAdd(&hist[bucket], 1);
+    atomicAdd(&hist[min(it.cost, PLAN_BUCKETS - 1)], 1);
   }
   __syncthreads();
 
-  // 3. Exclusive scan in decreasing-cost order: offset[c] = items with bucket > c.
-  if (tid == 0) {
-    int run = 0;
-    for (int c = PLAN_BUCKETS - 1; c >= 0; --c) {
-      const int h = hist[c];
-      hist[c] = run;
-      run += h;
+  // 3. Exclusive scan in decreasing-cost order: offset[c] = items with a larger bucket.
+  {
+    constexpr int PER = PLAN_BUCKETS / PLAN_THREADS;
+    int local[PER];
+    int sum = 0;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {  // thread tid owns buckets counted from the top
+      local[r] = hist[PLAN_BUCKETS - 1 - (tid * PER + r)];
+      sum += local[r];
+    }
+    scan_tmp[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < PLAN_THREADS; off <<= 1) {
+      const int add = tid >= off ? scan_tmp[tid - off] : 0;
+      __syncthreads();
+      scan_tmp[tid] += add;
+      __syncthreads();
+    }
+    int run = scan_tmp[tid] - sum;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      hist[PLAN_BUCKETS - 1 - (tid * PER + r)] = run;
+      run += local[r];
     }
   }
   __syncthreads();
@@ -110,8 +147,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     WorkItem it;
     describe(u, it);
     const int bucket = min(it.cost, PLAN_BUCKETS - 1);
-    const int pos = hist[bucket] + atomicAdd(&cursor[bucket], 1);
-    items[pos] = it;
+    items[hist[bucket] + atomicAdd(&cursor[bucket], 1)] = it;
   }
   if (tid == 0) *n_items = nitem;
 }

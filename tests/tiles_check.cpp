@@ -44,6 +44,15 @@ int main() {
               }
             }
             if (cnt != kt.count()) fail("count", mode, t0, t1, BK, cnt);
+            // the compile-time-mode instances walk the same tiles
+            for (int t = 0; t <= kt.last + 1; ++t) {
+              int a = -2, b = -2; bool ma = false, mb = false;
+              if (mode == MODE_FULL) { KeyTilesT<MODE_FULL> s(mode, p, t0, t1, BK); a = s.next(t); if (a >= 0) ma = s.needs_mask(a); }
+              else if (mode == MODE_STREAM) { KeyTilesT<MODE_STREAM> s(mode, p, t0, t1, BK); a = s.next(t); if (a >= 0) ma = s.needs_mask(a); }
+              else { KeyTilesT<MODE_BLOCK> s(mode, p, t0, t1, BK); a = s.next(t); if (a >= 0) ma = s.needs_mask(a); }
+              b = kt.next(t); if (b >= 0) mb = kt.needs_mask(b);
+              if (a != b || ma != mb) { fail("static-mode", mode, t0, t1, BK, t); break; }
+            }
             for (int i = t0; i <= t1; ++i)
               for (int j = 0; j <= i; ++j)
                 if (key_allowed(mode, p, i, j) && !vis[j / BK]) { fail("missed", mode, t0, t1, BK, j / BK); i = t1 + 1; break; }
