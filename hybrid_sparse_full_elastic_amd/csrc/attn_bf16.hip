@@ -9,24 +9,28 @@
 // Design for CDNA4:
 //  * One workgroup = one work item: a query tile of BT tokens times all G query heads of one
 //    KV head (rows r = token * G + head, so the K/V tile staged in LDS serves the whole GQA
-//    group), NW waves each owning NB blocks of 32 query rows.  The shipped configuration is
-//    8 waves x 1 block (256 rows): every wave fits in 256 VGPRs, so two waves share a SIMD and
-//    one wave's MFMAs overlap the other's softmax.
+//    group), 8 waves of 32 query rows.  Every wave fits in 256 VGPRs, so two waves share a
+//    SIMD.
 //  * S^T = K . Q^T with v_mfma_f32_32x32x16_bf16: every lane holds one query column, so the
-//    softmax row statistics are per-lane; only one cross-half swap (v_permlane32_swap) per
-//    tile is needed for the maximum.  Q stays in registers for the whole item.
+//    softmax row statistics are per-lane; one v_permlane32_swap per tile finishes the row
+//    maximum.  Q stays in registers for the whole item.
 //  * O^T = V^T . P^T: P^T comes straight from the S^T accumulators (bf16) with a fixed
-//    key-slot permutation; V is stored transposed in LDS with the same permutation, so the
-//    rescale of O by the running maximum is a per-lane multiply.
+//    key-slot permutation, and ds_read_b64_tr_b16 builds the matching V^T operand from the
+//    row-major V tile.  The rescale of O by the running maximum is a per-lane multiply.
 //  * Online softmax in the exp2 domain with the softmax scale and log2(e) folded into one
-//    multiply; fp32 accumulation throughout; masks are evaluated only on tiles that cross a
-//    causal, sink, window or block boundary, and tiles no query of the item may see are
-//    never loaded (streaming items cost O(sink + window), not O(n)).
-//  * Software pipeline per tile j: Q.K^T of tile j+1 is issued while exp2 of tile j runs,
-//    and P.V of tile j while tile j+1 is masked and reduced to its maximum.  The running
-//    maximum is raised lazily (only when a tile exceeds it by 2^8), so O is almost never
-//    rescaled.  K is staged two tiles ahead and V one tile ahead in double-buffered LDS
-//    slots; global loads run one more tile ahead in registers; one barrier per tile.
+//    FMA; fp32 accumulation throughout; the row sum adds the bf16 weights the P.V product
+//    uses (v_dot2) so numerator and denominator agree.  The running maximum is raised lazily
+//    (only when a tile exceeds it by 2^8), so O is almost never rescaled.
+//  * Masks are evaluated only on tiles that cross a causal, sink, window or block boundary,
+//    and tiles no query of the item may see are never loaded (streaming items cost
+//    O(sink + window), not O(n)).  Each item runs a loop compiled for its mode.
+//  * K/V tiles travel global -> LDS by buffer_load ... lds (no register staging) into three
+//    LDS slots each: K three tiles ahead, V two tiles ahead, so a load has two tile steps to
+//    land.  Rows past the sequence end read as zero through the buffer descriptor's range.
+//    Tiles are unpadded with XOR swizzles of the 16-byte chunks chosen so the K row reads
+//    and the transposing V reads are free of LDS bank conflicts.
+//  * Per tile step j: Q.K^T of tile j+1, exp2 of tile j, P.V of tile j, then the mask and
+//    maximum of tile j+1; one barrier per step.
 #include "elastic_internal.hpp"
 
 namespace elastic {
@@ -34,16 +38,19 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float LN2 = 0.69314718055994530942f;
+constexpr int NSLOT = 3;  // LDS slots per operand
 
-// x[lane] combined with x[lane ^ 32] by `op`; the swap returns both halves' values.
+// x[lane] combined with x[lane ^ 32]; the swap returns both halves' values.
 __device__ inline float half_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -53,17 +60,6 @@ __device__ inline float half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D>
-struct LdsTiles {
-  // Row strides in elements.  K rows: +8 spreads a wave's 16-byte row reads over all banks.
-  // V rows: +32 makes the four key rows of one transposing read start 16 banks apart, so
-  // each half-wave of ds_read_b64_tr_b16 touches every bank exactly once.
-  static constexpr int KST = D + 8;
-  static constexpr int VST = D + 32;
-  uint16_t k[2][BF16_BK * KST];
-  uint16_t v[2][BF16_BK * VST];
-};
-
 // max of three floats in one instruction (the inputs are never NaN here)
 __device__ inline float max3f(float a, float b, float c) {
   float r;
@@ -71,31 +67,49 @@ __device__ inline float max3f(float a, float b, float c) {
   return r;
 }
 
+// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding)
+#define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | 0x70 | 0xF00 | ((((n) >> 4) & 3) << 14))
+
+template <int D>
+struct LdsTiles {
+  uint16_t k[NSLOT][BF16_BK * D];
+  uint16_t v[NSLOT][BF16_BK * D];
+};
+
+// XOR swizzles of the 16-byte chunk index within a tile row (D/8 chunks per row).  K is read
+// 16 rows x one chunk at a time: consecutive rows must land in distinct 16-byte bank groups
+// of a 256-byte window.  V is read by ds_read_b64_tr_b16 as 4 rows x 4 chunks: each of the
+// 4 rows must shift the chunk group by 4 chunks.
+template <int D>
+__device__ __host__ constexpr int k_swizzle(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __host__ constexpr int v_swizzle(int row) {
+  return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+}
+
 // One work item with its mode known at compile time.
-template <int D, int NW, int NB, int MODE>
+template <int D, int MODE>
 __device__ __forceinline__ void attn_item(
     const WorkItem& it, LdsTiles<D>& lds, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
     float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens, int64_t total_tokens, int Hq,
     int Hkv, int G, int BT, float scale_log2, const Pattern& pat) {
-  constexpr int BK = BF16_BK, NT = NW * 64;
-  constexpr int DC = D / 16;   // 16-wide d chunks of Q.K^T
-  constexpr int DB = D / 32;   // 32-row d blocks of O^T
-  constexpr int KST = LdsTiles<D>::KST, VST = LdsTiles<D>::VST;
-  constexpr int KCH = (BK * D / 8 + NT - 1) / NT;       // 16-byte K chunks per thread
-  // Lazy rescaling: the running maximum is only raised when a tile's maximum exceeds it by
-  // more than 2^SLACK, so p = exp2(s - m) stays <= 2^SLACK and O is rarely rescaled.
-  constexpr float SLACK = 8.0f;
-  static_assert((BK * D / 8) % NT == 0 || NT > BK * D / 8, "K tile split");
+  constexpr int NW = BF16_NW, BK = BF16_BK, NT = NW * 64;
+  constexpr int DC = D / 16;          // 16-wide d chunks of Q.K^T
+  constexpr int DB = D / 32;          // 32-row d blocks of O^T
+  constexpr int CPR = D / 8;          // 16-byte chunks per tile row
+  constexpr int CPT = BK * CPR / NT;  // DMA chunks per thread per tile and operand
+  static_assert(CPT >= 1 && CPT * NT == BK * CPR, "tile split");
+  constexpr float SLACK = 8.0f;       // lazy rescale threshold (log2 units)
+  constexpr int SLOT = BK * D;        // elements per LDS slot
 
-  auto& k_lds = lds.k;
-  auto& v_lds = lds.v;
   const int64_t seq0 = cu_seqlens ? cu_seqlens[it.seq] : 0;
   const int n = cu_seqlens ? cu_seqlens[it.seq + 1] - (int)seq0 : (int)total_tokens;
   const int t0 = it.qtile * BT;
   const int t1 = min(t0 + BT, n) - 1;
   const int g = it.group;
-  constexpr int mode = MODE;
   const KeyTilesT<MODE> tiles(MODE, pat, t0, t1, BK);
   const int blk_shift = 31 - __clz(pat.block);  // block sizes are powers of two
 
@@ -105,264 +119,225 @@ __device__ __forceinline__ void attn_item(
   const uint16_t* kbase = k + seq0 * kv_row + (int64_t)g * D;
   const uint16_t* vbase = v + seq0 * kv_row + (int64_t)g * D;
   const float c = scale_log2;
-  // source address of this lane in a transposing V read: key (l/4) + 4*half of the 16-key
-  // chunk, columns (group parity)*16 + 4*(l%4) of the 32-column d block
-  const int v_lane_off = ((lane & 15) / 4 + 4 * half) * VST + ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
 
-  // ---- this lane's query rows: r = token * G + head inside the item
-  int qi[NB], qhead[NB];
-  bool qvalid[NB];
-  bf16x8 qreg[NB][DC];
+  // ---- this lane's query row: r = token * G + head inside the item
+  const int r = wave * 32 + l32;
+  const int tl = r / G;
+  const int qi = t0 + tl;
+  const int qhead = g * G + (r - tl * G);
+  const bool qvalid = tl < BT && qi <= t1;
+  const int qblk = qi >> blk_shift;
+  bf16x8 qreg[DC];
+  if (qvalid) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + ((seq0 + qi) * Hq + qhead) * (int64_t)D + half * 8);
 #pragma unroll
-  for (int qb = 0; qb < NB; ++qb) {
-    const int r = (wave * NB + qb) * 32 + l32;
-    const int tl = r / G;
-    const int hh = r - tl * G;
-    qi[qb] = t0 + tl;
-    qhead[qb] = g * G + hh;
-    qvalid[qb] = tl < BT && qi[qb] <= t1;
-    if (qvalid[qb]) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(
-          q + ((seq0 + qi[qb]) * Hq + qhead[qb]) * (int64_t)D + half * 8);
+    for (int dc = 0; dc < DC; ++dc) qreg[dc] = __builtin_bit_cast(bf16x8, src[dc * 2]);
+  } else {
 #pragma unroll
-      for (int dc = 0; dc < DC; ++dc) qreg[qb][dc] = __builtin_bit_cast(bf16x8, src[dc * 2]);
-    } else {
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) qreg[qb][dc] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-    }
+    for (int dc = 0; dc < DC; ++dc) qreg[dc] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
   }
 
-  // ---- K/V tile staging: global -> registers -> LDS, both row-major [key][d]
-  u32x4 kreg[KCH];
-  u32x4 vreg[KCH];
-  // Raw buffer loads: a per-tile descriptor covers only the tile's rows that exist in the
-  // sequence, so rows past its end read as zero without branches.
+  // ---- DMA staging.  Instruction m of wave w fills LDS chunks [(w*CPT+m)*64, +64) of a tile;
+  // lane i's chunk P holds row P/CPR, logical chunk (P%CPR) ^ swizzle(row).
+  int k_voff[CPT], v_voff[CPT];
+#pragma unroll
+  for (int m = 0; m < CPT; ++m) {
+    const int P = (wave * CPT + m) * 64 + lane;
+    const int row = P / CPR, pc = P % CPR;
+    k_voff[m] = (row * (int)kv_row + (pc ^ k_swizzle<D>(row)) * 8) * 2;
+    v_voff[m] = (row * (int)kv_row + (pc ^ v_swizzle<D>(row)) * 8) * 2;
+  }
   auto tile_rsrc = [&](const uint16_t* base, int kt) {
     const int rows = min(n - kt * BK, BK);
-    return __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(base + (int64_t)kt * BK * kv_row), (short)0,
-        rows * (int)kv_row * 2, 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + (int64_t)kt * BK * kv_row),
+                                             (short)0, rows * (int)kv_row * 2, 0x00020000);
   };
-  auto load_tile = [&](const uint16_t* base, int kt, u32x4 (&reg)[KCH]) {
+  auto dma = [&](const uint16_t* base, int kt, uint16_t* slot, const int (&voff)[CPT]) {
     const auto rs = tile_rsrc(base, kt);
 #pragma unroll
-    for (int cc = 0; cc < KCH; ++cc) {
-      const int idx = tid + cc * NT;
-      const int row = idx / (D / 8), col8 = idx % (D / 8);
-      if (idx < BK * D / 8)
-        reg[cc] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (row * (int)kv_row + col8 * 8) * 2, 0, 0));
-    }
+    for (int m = 0; m < CPT; ++m)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(slot + (wave * CPT + m) * 512), 16,
+                                               voff[m], 0, 0, 0);
   };
-  auto load_k = [&](int kt) { load_tile(kbase, kt, kreg); };
-  auto load_v = [&](int kt) { load_tile(vbase, kt, vreg); };
-  auto store_tile = [&](uint16_t* dst, int stride, const u32x4 (&reg)[KCH]) {
+
+  // ---- LDS read offsets (elements), loop-invariant per lane
+  // K: row kb*32 + l32, logical chunk dc*2 + half
+  int k_roff[DC];
 #pragma unroll
-    for (int cc = 0; cc < KCH; ++cc) {
-      const int idx = tid + cc * NT;
-      const int row = idx / (D / 8), col8 = idx % (D / 8);
-      if (idx < BK * D / 8) *reinterpret_cast<u32x4*>(dst + row * stride + col8 * 8) = reg[cc];
-    }
-  };
-  auto store_k = [&](int buf) { store_tile(&k_lds[buf][0], KST, kreg); };
-  auto store_v = [&](int buf) { store_tile(&v_lds[buf][0], VST, vreg); };
+  for (int dc = 0; dc < DC; ++dc) k_roff[dc] = l32 * D + (((dc * 2 + half) ^ k_swizzle<D>(l32)) * 8);
+  // V (transposing read): source row 4*half + (lane&15)/4 of a 16-key chunk, columns
+  // db*32 + ((lane>>4)&1)*16 + 4*(lane&3) .. +3
+  int v_roff[DB];
+  {
+    const int s = lane & 15;
+    const int row0 = 4 * half + (s >> 2);
+    const int cl = ((lane >> 4) & 1) * 2 + ((s & 3) >> 1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      v_roff[db] = row0 * D + (((db * 4 + cl) ^ v_swizzle<D>(row0)) * 8) + (s & 1) * 4;
+  }
 
   // ---- S^T[key, query] = K . Q^T for the two 32-key halves of a tile
-  auto qk = [&](int buf, f32x16 (&s)[2][NB]) {
-    const uint16_t* ks = &k_lds[buf][0];
+  auto qk = [&](const uint16_t* ks, f32x16 (&s)[2]) {
     const f32x16 zero = {};
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
       bf16x8 a[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        a[kb] = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + l32) * KST + dc * 16 + half * 8);
+        a[kb] = *reinterpret_cast<const bf16x8*>(ks + kb * 32 * D + k_roff[dc]);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < NB; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], qreg[qb][dc],
-                                                             dc == 0 ? zero : s[kb][qb], 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], qreg[dc], dc == 0 ? zero : s[kb], 0, 0, 0);
     }
   };
 
-  // ---- masks: allowed(j) = j <= hi && (j < a || j >= b), exact per (query, key)
-  int qblk[NB];
-#pragma unroll
-  for (int qb = 0; qb < NB; ++qb) qblk[qb] = qi[qb] >> blk_shift;
-  auto apply_mask = [&](f32x16 (&s)[2][NB], int kt) {
-    const int kblk = (kt * BK) >> blk_shift;  // one key block per tile (block % BK == 0)
-    const bool kvis_static = kblk < pat.sink_blocks ||
-                             (pat.stride_blocks > 0 && kblk % pat.stride_blocks == 0);
-#pragma unroll
-    for (int qb = 0; qb < NB; ++qb) {
-      const int i = qi[qb];
-      const int hi = qvalid[qb] ? i : -1;
-      int a = 0, b = 0;
-      if (mode == MODE_STREAM) {
-        a = pat.sink;
-        b = i - pat.window + 1;
-      } else if (mode == MODE_BLOCK) {
-        b = (kvis_static || qblk[qb] - kblk <= pat.local_blocks) ? 0 : 0x7fffffff;
-      }
-      const int base = kt * BK + half * 4;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int j = base + kb * 32 + (e >> 2) * 8 + (e & 3);
-          const bool ok = j <= hi && (j < a || j >= b);
-          if (!ok) s[kb][qb][e] = -__builtin_huge_valf();
-        }
+  // ---- exact masks on edge tiles: allowed(j) = j <= hi && (j < a || j >= b)
+  auto apply_mask = [&](f32x16 (&s)[2], int kt) {
+    const int hi = qvalid ? qi : -1;
+    int a = 0, b = 0;
+    if (MODE == MODE_STREAM) {
+      a = pat.sink;
+      b = qi - pat.window + 1;
+    } else if (MODE == MODE_BLOCK) {
+      const int kblk = (kt * BK) >> blk_shift;  // one key block per tile (block % BK == 0)
+      const bool vis = kblk < pat.sink_blocks || qblk - kblk <= pat.local_blocks ||
+                       (pat.stride_blocks > 0 && kblk % pat.stride_blocks == 0);
+      b = vis ? 0 : 0x7fffffff;
     }
-  };
-  auto tile_max = [&](f32x16 (&s)[2][NB], float (&mt)[NB]) {
+    const int base = kt * BK + half * 4;
 #pragma unroll
-    for (int qb = 0; qb < NB; ++qb) {
-      float m0 = max3f(s[0][qb][0], s[1][qb][0], s[0][qb][1]);
-      float m1 = max3f(s[1][qb][1], s[0][qb][2], s[1][qb][2]);
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 3; e < 15; e += 2) {
-        m0 = max3f(m0, s[0][qb][e], s[1][qb][e]);
-        m1 = max3f(m1, s[0][qb][e + 1], s[1][qb][e + 1]);
+      for (int e = 0; e < 16; ++e) {
+        const int j = base + kb * 32 + (e >> 2) * 8 + (e & 3);
+        if (!(j <= hi && (j < a || j >= b))) s[kb][e] = -__builtin_huge_valf();
       }
-      mt[qb] = half_max(max3f(m0, m1, max3f(s[0][qb][15], s[1][qb][15], m0)));
-    }
   };
 
   // ---- running state (m in the scaled log2 domain)
-  f32x16 oacc[DB][NB];
-  float m_sc[NB], l_run[NB], alpha[NB];
+  f32x16 oacc[DB];
 #pragma unroll
-  for (int qb = 0; qb < NB; ++qb) {
-    m_sc[qb] = -1.0e30f;  // finite: fully masked tiles give p = 0 and never raise it
-    l_run[qb] = 0.f;
-    alpha[qb] = 1.f;
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[db][qb][e] = 0.f;
-  }
-  bool pending = false;  // wave-uniform: O and l wait for a multiply by alpha
+    for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+  float m_sc = -1.0e30f;  // finite: fully masked tiles give p = 0 and never raise it
+  float l_run = 0.f, alpha = 1.f;
+  bool pending = false;   // wave-uniform: O and l wait for a multiply by alpha
 
-  // Raise the running maximum for the scores in s (raw, masked); decide the rescale.
-  auto update_max = [&](f32x16 (&s)[2][NB]) {
-    float mt[NB];
-    tile_max(s, mt);
-    bool need = false;
-    float mn[NB];
+  auto update_max = [&](f32x16 (&s)[2]) {
+    float m0 = max3f(s[0][0], s[1][0], s[0][1]);
+    float m1 = max3f(s[1][1], s[0][2], s[1][2]);
 #pragma unroll
-    for (int qb = 0; qb < NB; ++qb) {
-      const float ms = mt[qb] * c;
-      need |= ms > m_sc[qb] + SLACK;
-      mn[qb] = fmaxf(m_sc[qb], ms);
+    for (int e = 3; e < 15; e += 2) {
+      m0 = max3f(m0, s[0][e], s[1][e]);
+      m1 = max3f(m1, s[0][e + 1], s[1][e + 1]);
     }
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-      for (int qb = 0; qb < NB; ++qb) {
-        alpha[qb] = __builtin_amdgcn_exp2f(m_sc[qb] - mn[qb]);
-        m_sc[qb] = mn[qb];
-      }
+    const float ms = half_max(max3f(m0, m1, max3f(s[0][15], s[1][15], m0))) * c;
+    if (__builtin_amdgcn_ballot_w64(ms > m_sc + SLACK) != 0) {
+      const float mn = fmaxf(m_sc, ms);
+      alpha = __builtin_amdgcn_exp2f(m_sc - mn);
+      m_sc = mn;
       pending = true;
     }
   };
 
-  // ---- tile schedule: kt_cur = tile j, kt_n1 = j+1, kt_n2 = j+2
+  // ---- tile schedule: kt_cur = tile j, kt_n1/2/3 = tiles j+1..j+3 (-1 when absent)
   int kt_cur = tiles.next(0);
   if (kt_cur < 0) return;  // cannot happen: the diagonal tile is always visited
   int kt_n1 = tiles.next(kt_cur + 1);
   int kt_n2 = kt_n1 >= 0 ? tiles.next(kt_n1 + 1) : -1;
+  int kt_n3 = kt_n2 >= 0 ? tiles.next(kt_n2 + 1) : -1;
 
-  // prologue: tile 0 (K and V) and K of tile 1 into LDS; registers hold K_2 and V_1
-  load_k(kt_cur);
-  load_v(kt_cur);
-  store_k(0);
-  store_v(0);
+  // prologue: K_0..K_2 and V_0, V_1 land; S_0 computed and reduced
+  uint16_t* kslot = &lds.k[0][0];
+  uint16_t* vslot = &lds.v[0][0];
+  dma(kbase, kt_cur, kslot, k_voff);
+  dma(vbase, kt_cur, vslot, v_voff);
   if (kt_n1 >= 0) {
-    load_k(kt_n1);
-    load_v(kt_n1);
-    store_k(1);
+    dma(kbase, kt_n1, kslot + SLOT, k_voff);
+    dma(vbase, kt_n1, vslot + SLOT, v_voff);
   }
-  if (kt_n2 >= 0) load_k(kt_n2);
+  if (kt_n2 >= 0) dma(kbase, kt_n2, kslot + 2 * SLOT, k_voff);
+  WAIT_VMCNT(0);
   __syncthreads();
-  f32x16 s0[2][NB], s1[2][NB];
-  qk(0, s0);
-  __syncthreads();  // every wave is done with K slot 0 before it is refilled
+  f32x16 s0[2], s1[2];
+  qk(kslot, s0);
+  __syncthreads();  // every wave is done with K slot 0 before step 0 refills it
   if (tiles.needs_mask(kt_cur)) apply_mask(s0, kt_cur);
   update_max(s0);
   pending = false;  // O and l are still zero
-  int slot = 0;
+  int sj = 0;       // LDS slot of tile j (tile t lives in slot t mod 3)
 
-  // One pipelined step on tile j: Q.K^T of tile j+1 and exp of tile j, then P.V of tile j
-  // and the mask / maximum of tile j+1; LDS refills of K_{j+2} and V_{j+1}; global loads of
-  // K_{j+3} and V_{j+2}; one barrier.
-  auto step = [&](f32x16 (&sc)[2][NB], f32x16 (&sn)[2][NB]) {
+  // One step on tile j: DMA K_{j+3} and V_{j+2}; S_{j+1} = K_{j+1} Q^T; p_j = exp2(c s_j - m);
+  // O += V_j^T P_j^T; mask and maximum of S_{j+1}; wait for the previous step's DMA; barrier.
+  auto step = [&](f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    const int sj1 = sj == NSLOT - 1 ? 0 : sj + 1;
+    const int sj2 = sj1 == NSLOT - 1 ? 0 : sj1 + 1;
+    const int n_dma = (kt_n3 >= 0 ? CPT : 0) + (kt_n2 >= 0 ? CPT : 0);
+    if (kt_n3 >= 0) dma(kbase, kt_n3, kslot + sj * SLOT, k_voff);   // slot of K_j, read last step
+    if (kt_n2 >= 0) dma(vbase, kt_n2, vslot + sj2 * SLOT, v_voff);  // slot of V_{j-1}, read last step
     if (pending) {
+      l_run *= alpha;
 #pragma unroll
-      for (int qb = 0; qb < NB; ++qb) {
-        l_run[qb] *= alpha[qb];
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[db][qb][e] *= alpha[qb];
-      }
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
       pending = false;
     }
     const bool has_next = kt_n1 >= 0;
-    // phase A: S_{j+1} (MFMA) while p_j = exp2(c s_j - m) (VALU)
-    qk(slot ^ 1, sn);
-    bf16x8 pop[2][2][NB];
-    float lsum4[NB][4];
+    qk(kslot + sj1 * SLOT, sn);
+    bf16x8 pop[2][2];
+    const float nm = -m_sc;
 #pragma unroll
-    for (int qb = 0; qb < NB; ++qb) {
-      lsum4[qb][0] = lsum4[qb][1] = lsum4[qb][2] = lsum4[qb][3] = 0.f;
-      const float nm = -m_sc[qb];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int e = 0; e < 16; ++e)
+        pop[kb][e >> 3][e & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[kb][e], c, nm));
+    // row sum of the bf16 weights the P.V product actually uses, two per v_dot2
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][qb][e], c, nm));
-          lsum4[qb][e & 3] += p;
-          pop[kb][e >> 3][qb][e & 7] = (__bf16)p;
-        }
-    }
-    // phase B: O^T += V^T P^T (MFMA) while l += sum p and the next tile's max (VALU)
-    // V^T A-operands straight from the row-major V tile: ds_read_b64_tr_b16 hands lane
-    // (16-lane group gr, index l) V[key_i][dbase + l] for the four keys key_i its group's
-    // source lanes point at; two reads give the 8 key slots of the MFMA lane.
-    const uint16_t* vs = &v_lds[slot][0] + v_lane_off;
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int pr = 0; pr < 4; ++pr)
+          ls[pr] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pop[kb][cc][2 * pr], pop[kb][cc][2 * pr + 1]},
+                                                   ones, ls[pr], false);
+    // V^T operands: ds_read_b64_tr_b16 gives lane (16-lane group, index l) the values
+    // V[key_i][dbase + l] for the four keys its group's source lanes point at
+    const uint16_t* vs = vslot + sj * SLOT;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-          const uint16_t* src = vs + (kb * 32 + cc * 16) * VST + db * 32;
+          const uint16_t* src = vs + v_roff[db] + (kb * 32 + cc * 16) * D;
           const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 8 * VST));
-          const bf16x8 a = __builtin_bit_cast(
-              bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-#pragma unroll
-          for (int qb = 0; qb < NB; ++qb)
-            oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[kb][cc][qb], oacc[db][qb], 0, 0, 0);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 8 * D));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[kb][cc], oacc[db], 0, 0, 0);
         }
-#pragma unroll
-    for (int qb = 0; qb < NB; ++qb)
-      l_run[qb] += (lsum4[qb][0] + lsum4[qb][1]) + (lsum4[qb][2] + lsum4[qb][3]);
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     if (has_next) {
       if (tiles.needs_mask(kt_n1)) apply_mask(sn, kt_n1);
       update_max(sn);
     }
-    if (kt_n2 >= 0) store_k(slot);
-    if (has_next) store_v(slot ^ 1);
-    const int kt_n3 = kt_n2 >= 0 ? tiles.next(kt_n2 + 1) : -1;
-    if (kt_n3 >= 0) load_k(kt_n3);
-    if (kt_n2 >= 0) load_v(kt_n2);
-    __syncthreads();
+    const int kt_n4 = kt_n3 >= 0 ? tiles.next(kt_n3 + 1) : -1;
+    // this step's DMA may stay in flight; the previous step's (K_{j+2}, V_{j+1}) must land
+    if (n_dma == 2 * CPT) WAIT_VMCNT(2 * CPT);
+    else if (n_dma == CPT) WAIT_VMCNT(CPT);
+    else WAIT_VMCNT(0);
+    // LDS reads of this step done, then the barrier.  (__syncthreads would also wait for the
+    // DMA issued this step, which must stay in flight.)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     kt_cur = kt_n1;
     kt_n1 = kt_n2;
     kt_n2 = kt_n3;
-    slot ^= 1;
+    kt_n3 = kt_n4;
+    sj = sj1;
   };
 
   while (true) {
@@ -373,61 +348,46 @@ __device__ __forceinline__ void attn_item(
   }
 
   // ---- epilogue: normalise, store bf16 O (and the natural-log LSE)
+  const float lt = half_sum(l_run);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  if (!qvalid) return;
+  uint16_t* dst = o + ((seq0 + qi) * Hq + qhead) * (int64_t)D;
 #pragma unroll
-  for (int qb = 0; qb < NB; ++qb) {
-    const float lt = half_sum(l_run[qb]);
-    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    if (!qvalid[qb]) continue;
-    uint16_t* dst = o + ((seq0 + qi[qb]) * Hq + qhead[qb]) * (int64_t)D;
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int ig = 0; ig < 4; ++ig) {
+      bf16x4 w;
 #pragma unroll
-      for (int ig = 0; ig < 4; ++ig) {
-        bf16x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[db][qb][ig * 4 + e] * inv);
-        *reinterpret_cast<u32x2*>(dst + db * 32 + ig * 8 + half * 4) = __builtin_bit_cast(u32x2, w);
-      }
-    if (lse != nullptr && half == 0)
-      lse[(int64_t)qhead[qb] * total_tokens + seq0 + qi[qb]] = (m_sc[qb] + __log2f(lt)) * LN2;
-  }
+      for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[db][ig * 4 + e] * inv);
+      *reinterpret_cast<u32x2*>(dst + db * 32 + ig * 8 + half * 4) = __builtin_bit_cast(u32x2, w);
+    }
+  if (lse != nullptr && half == 0)
+    lse[(int64_t)qhead * total_tokens + seq0 + qi] = (m_sc + __log2f(lt)) * LN2;
 }
 
-template <int D, int NW, int NB>
-__global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(
+template <int D>
+__global__ __launch_bounds__(BF16_NW * 64, 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens,
     int64_t total_tokens, int Hq, int Hkv, int G, int BT, float scale_log2,
     const int32_t* __restrict__ head_mask, Pattern pat, const WorkItem* __restrict__ items,
     const int32_t* __restrict__ n_items) {
-  __shared__ __attribute__((aligned(16))) LdsTiles<D> lds;
+  __shared__ __attribute__((aligned(1024))) LdsTiles<D> lds;
   if ((int)blockIdx.x >= *n_items) return;
   const WorkItem it = items[blockIdx.x];
   const bool full = head_mask == nullptr || head_mask[it.seq * Hkv + it.group] != 0;
   if (full)
-    attn_item<D, NW, NB, MODE_FULL>(it, lds, q, k, v, o, lse, cu_seqlens, total_tokens, Hq, Hkv, G,
-                                    BT, scale_log2, pat);
+    attn_item<D, MODE_FULL>(it, lds, q, k, v, o, lse, cu_seqlens, total_tokens, Hq, Hkv, G, BT,
+                            scale_log2, pat);
   else if (pat.kind == ELASTIC_SPARSE_STREAMING)
-    attn_item<D, NW, NB, MODE_STREAM>(it, lds, q, k, v, o, lse, cu_seqlens, total_tokens, Hq, Hkv,
-                                      G, BT, scale_log2, pat);
+    attn_item<D, MODE_STREAM>(it, lds, q, k, v, o, lse, cu_seqlens, total_tokens, Hq, Hkv, G, BT,
+                              scale_log2, pat);
   else
-    attn_item<D, NW, NB, MODE_BLOCK>(it, lds, q, k, v, o, lse, cu_seqlens, total_tokens, Hq, Hkv,
-                                     G, BT, scale_log2, pat);
+    attn_item<D, MODE_BLOCK>(it, lds, q, k, v, o, lse, cu_seqlens, total_tokens, Hq, Hkv, G, BT,
+                             scale_log2, pat);
 }
 
 }  // namespace
-
-template <int D, int NW, int NB>
-static void launch_cfg(int64_t grid, hipStream_t stream, const void* q, const void* k, const void* v,
-                       void* o, float* lse, const int32_t* cu_seqlens, int64_t total_tokens,
-                       int n_q_heads, int n_kv_heads, int G, int BT, float scale_log2,
-                       const int32_t* head_mask, const Pattern& pat, const WorkItem* items,
-                       const int32_t* n_items) {
-  hipLaunchKernelGGL((attn_bf16_kernel<D, NW, NB>), dim3((unsigned)grid), dim3(NW * 64), 0, stream,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
-                     cu_seqlens, total_tokens, n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask,
-                     pat, items, n_items);
-}
 
 hipError_t launch_attn_bf16(int head_dim, const void* q, const void* k, const void* v, void* o,
                             float* lse, const int32_t* cu_seqlens, int64_t total_tokens,
@@ -438,13 +398,15 @@ hipError_t launch_attn_bf16(int head_dim, const void* q, const void* k, const vo
   const int G = n_q_heads / n_kv_heads;
   if (grid <= 0) return hipSuccess;
   if (head_dim == 128)
-    launch_cfg<128, BF16_NW, BF16_NB>(grid, stream, q, k, v, o, lse, cu_seqlens, total_tokens,
-                                      n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask, pat,
-                                      items, n_items);
+    hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3((unsigned)grid), dim3(BF16_NW * 64), 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
+                       cu_seqlens, total_tokens, n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask,
+                       pat, items, n_items);
   else
-    launch_cfg<64, BF16_NW, BF16_NB>(grid, stream, q, k, v, o, lse, cu_seqlens, total_tokens,
-                                     n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask, pat,
-                                     items, n_items);
+    hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3((unsigned)grid), dim3(BF16_NW * 64), 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
+                       cu_seqlens, total_tokens, n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask,
+                       pat, items, n_items);
   return hipGetLastError();
 }
 
