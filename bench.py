@@ -33,7 +33,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
     p.add_argument("--no-supplements", action="store_true")
-    p.add_argument("--scaling", action="store_true", help="streaming-window and length scaling sweep")
+    p.add_argument("--no-scaling", action="store_true",
+                   help="skip the streaming-head scaling sweeps (length and window)")
     p.add_argument("--copy-probe", action="store_true",
                    help="run one plain 1 GiB device-to-device copy first (calibrates HBM byte counters)")
     return p.parse_args()
@@ -158,17 +159,40 @@ def main():
             "note": "attn_ms brackets elastic_attn_prefill = scheduler (one small kernel) + attention kernel",
         },
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic(w.name)},
         "input_gen_s": round(gen_s, 2),
     }
 
     if not args.no_supplements:
         rec["supplements"] = supplements(ext, torch, w, q, k, v, o, cu, ws_attn, stream, args)
+        del q, k, v, o
+        if has_router:
+            del hidden
+        torch.cuda.empty_cache()
+        if not args.no_scaling:
+            rec["supplements"]["streaming_scaling"] = streaming_scaling(ext, torch, stream)
 
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, data, mask_h, args.cpu_seconds)
 
     print(json.dumps(rec), flush=True)
+
+
+def recorded_traffic(workload):
+    """HBM bytes per attention launch from the committed FETCH_SIZE / WRITE_SIZE counter
+    summary, or None when the kernel source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"attn_bf16_kernel-{workload}.pmc.txt")
+    src = os.path.join(ROOT, "hybrid_sparse_full_elastic_amd", "csrc", "attn_bf16.hip")
+    if not os.path.exists(path):
+        return None
+    fields = dict(line.split(": ", 1) for line in open(path).read().splitlines()
+                  if line and not line.startswith("#") and ": " in line)
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if fields.get("attn_source_sha256_16") != digest:
+        return None
+    return int(float(fields["traffic_bytes_per_launch"]))
 
 
 def _time_attn(ext, torch, stream, fn, reps=10, warm=3):
@@ -199,6 +223,50 @@ def supplements(ext, torch, w, q, k, v, o, cu, ws, stream, args):
     flops_s = 4 * D * ext.attn_entries(list(w.seqlens), all_sparse.cpu().numpy(), hq, hkv, w.sparse)
     out["sparse_heads_only"] = {"attn_ms": round(ms_s, 4), "tflops": round(flops_s / ms_s / 1e9, 2)}
     return out
+
+
+def streaming_scaling(ext, torch, stream):
+    """All heads streaming (32 query / 8 KV heads, D 128): time per allowed entry across
+    sequence lengths (sink 128 + window 1024), and time against window size at 64K.  Inputs
+    are prefixes of one seeded 131K-token draw."""
+    from synth import inputs as syn
+    nmax, hq, hkv, D = 131072, 32, 8, 128
+    dev = "cuda:0"
+
+    def dev_bits(seed, tag, shape):
+        x = syn.draw_bf16_bits(seed, tag, shape, 0.5)
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q = dev_bits(7, 0, (nmax, hq, D))
+    k = dev_bits(7, 1, (nmax, hkv, D))
+    v = dev_bits(7, 2, (nmax, hkv, D))
+    o = torch.empty_like(q)
+    ws = torch.empty(ext.attn_workspace_size(0, 1, nmax, hq, hkv, D), dtype=torch.uint8, device=dev)
+    sparse_mask = torch.zeros((1, hkv), dtype=torch.int32, device=dev)
+
+    def run(n, sparse):
+        qs, ks, vs, os_ = q[:n], k[:n], v[:n], o[:n]
+        ms = _time_attn(ext, torch, stream, lambda: ext.attn_prefill(
+            qs, ks, vs, max_seqlen=n, head_mask=sparse_mask, sparse=sparse, out=os_, workspace=ws))
+        entries = ext.attn_entries([n], [[0] * hkv], hq, hkv, sparse)
+        return ms, entries
+
+    by_len = []
+    sp = {"kind": "streaming", "sink": 128, "window": 1024}
+    for n in (8192, 16384, 32768, 65536, 131072):
+        ms, e = run(n, sp)
+        by_len.append({"n": n, "ms": round(ms, 4), "ns_per_kentry": round(ms * 1e6 / (e / 1e3), 4)})
+    per = [r["ns_per_kentry"] for r in by_len]
+    by_win = []
+    for wdw in (512, 1024, 2048, 4096):
+        ms, e = run(65536, {"kind": "streaming", "sink": 128, "window": wdw})
+        by_win.append({"window": wdw, "ms": round(ms, 4)})
+    ratios = [round(by_win[i + 1]["ms"] / by_win[i]["ms"], 3) for i in range(len(by_win) - 1)]
+    return {"by_length_sink128_window1024": by_len,
+            "time_per_entry_spread": round(max(per) / min(per) - 1.0, 4),
+            "length_check_pass": max(per) / min(per) - 1.0 <= 0.20,
+            "by_window_64k": by_win, "window_doubling_ratios": ratios,
+            "window_check_pass": all(1.6 <= r <= 2.2 for r in ratios)}
 
 
 def cpu_baseline(w, data, mask_h, target_s):

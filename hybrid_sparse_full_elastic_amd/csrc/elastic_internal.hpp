@@ -113,9 +113,20 @@ struct KeyTilesT {
       const int wb = win_begin > se ? win_begin : se;
       return se + (last >= wb ? last - wb + 1 : 0);
     }
-    int c = 0;
-    for (int kt = next(0); kt >= 0; kt = next(kt + 1)) ++c;
-    return c;
+    // block: every tile of each visible key block below qb1, plus the diagonal block's tiles
+    // up to `last`.  Visible blocks below qb1: [0, sink) U [qb0 - local, qb1) U stride
+    // multiples, counted without enumeration.
+    const int a = p.sink_blocks < qb1 ? p.sink_blocks : qb1;
+    const int b0 = qb0 - p.local_blocks > 0 ? qb0 - p.local_blocks : 0;
+    int nb;
+    if (a >= b0) {
+      nb = qb1;
+    } else {
+      nb = a + (qb1 - b0);
+      if (p.stride_blocks > 0)
+        nb += (b0 + p.stride_blocks - 1) / p.stride_blocks - (a + p.stride_blocks - 1) / p.stride_blocks;
+    }
+    return nb * tpb + (last - qb1 * tpb + 1);
   }
 };
 using KeyTiles = KeyTilesT<-1>;
@@ -160,6 +171,7 @@ hipError_t launch_route(const void* hidden, int hidden_dtype, const int32_t* cu_
                         int64_t total_tokens, int d_model, int pool_head, int pool_tail,
                         const float* w1, int d_router, const float* w2, int n_kv_heads,
                         float threshold, float* logits_out, int32_t* mask_out, float* partials,
-                        int64_t max_slabs, float* pooled, float* zbuf, hipStream_t stream);
+                        int64_t max_slabs, float* zpart, int32_t* counters, hipStream_t stream);
+constexpr int ROUTE_HCOLS = 64;  // columns per route_head workgroup
 
 }  // namespace elastic

@@ -9,8 +9,9 @@
 //
 // Pooling streams hidden[T, d] once from HBM and dominates the router's time, so it is
 // written for bandwidth: many workgroups, each summing a slab of up to ROUTE_SLAB rows of a
-// 512-column strip with 16-byte loads (4 waves interleave rows), then fixed-order
-// reductions.  No floating-point atomics anywhere: results are bitwise reproducible.
+// 512-column strip with 16-byte loads (4 waves interleave rows, 4 rows in flight per lane).
+// A second kernel finishes the mean, the MLP and the threshold.  No floating-point atomics
+// anywhere: every sum runs in a fixed order, so results are bitwise reproducible.
 #include "elastic_internal.hpp"
 
 namespace elastic {
@@ -18,7 +19,6 @@ namespace {
 
 constexpr int RT = 256;          // threads per workgroup
 constexpr int RCOLS = 512;       // columns per pooling workgroup: 64 lanes x 8
-constexpr int FIN_COLS = 64;     // columns per finishing workgroup
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -69,9 +69,12 @@ __device__ inline void load8(const void* hidden, int dtype, int64_t off, float* 
 // Partial column sums of one slab: partials[slab, col].
 __global__ __launch_bounds__(RT) void route_pool_partial(
     const void* __restrict__ hidden, int dtype, const int32_t* __restrict__ cu, int batch,
-    int64_t total, int d, int pool_head, int pool_tail, float* __restrict__ partials) {
+    int64_t total, int d, int pool_head, int pool_tail, float* __restrict__ partials,
+    int32_t* __restrict__ counters) {
   __shared__ float red[3][64][8 + 1];
   const int slab = blockIdx.x;
+  if (slab == 0 && blockIdx.y == 0)  // completion counters of route_head start at zero
+    for (int b = threadIdx.x; b < batch; b += RT) counters[b] = 0;
   int b = -1, slab_in = 0, acc = 0;
   SeqPool s{};
   for (int bb = 0; bb < batch; ++bb) {
@@ -124,87 +127,107 @@ __global__ __launch_bounds__(RT) void route_pool_partial(
   }
 }
 
-// pooled[b, col] = (sum over the slabs of sequence b) / pooled rows.
-__global__ __launch_bounds__(RT) void route_pool_finish(
+// route_head: workgroup (b, ch) finishes the mean of sequence b over HCOLS columns (the
+// sequence's slab partials summed in slab order), multiplies that strip into every row of W1
+// (partial z), and the last workgroup of the sequence to finish sums the partial z in strip
+// order, applies ReLU and W2 and thresholds the logits.  Completion is counted with one
+// integer atomic per sequence; all floating-point sums run in a fixed order.
+constexpr int HCOLS = ROUTE_HCOLS;
+constexpr int HT = 1024;          // threads of route_head: 16 waves split a sequence's slabs
+constexpr int HW = HT / 64;
+
+__global__ __launch_bounds__(HT) void route_head(
     const float* __restrict__ partials, const int32_t* __restrict__ cu, int batch, int64_t total,
-    int d, int pool_head, int pool_tail, float* __restrict__ pooled) {
-  __shared__ float red[4][FIN_COLS];
-  const int b = blockIdx.x;
+    int d, int pool_head, int pool_tail, const float* __restrict__ w1, int d_router,
+    const float* __restrict__ w2, int n_kv_heads, float threshold, float* __restrict__ zpart,
+    int32_t* __restrict__ counters, float* __restrict__ logits, int32_t* __restrict__ mask) {
+  __shared__ float red[HW][HCOLS];
+  __shared__ float hbar[HCOLS];
+  __shared__ float zs[ROUTE_MAX_DR];
+  __shared__ int is_last;
+  const int b = blockIdx.x, ch = blockIdx.y, nch = gridDim.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int first = 0;
   for (int bb = 0; bb < b; ++bb) {
     const SeqPool s = seq_pool(cu, bb, total, pool_head, pool_tail);
     first += (s.m + ROUTE_SLAB - 1) / ROUTE_SLAB;
   }
-  const SeqPool s = seq_pool(cu, b, total, pool_head, pool_tail);
-  const int ns = (s.m + ROUTE_SLAB - 1) / ROUTE_SLAB;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = blockIdx.y * FIN_COLS + lane;
+  const SeqPool sp = seq_pool(cu, b, total, pool_head, pool_tail);
+  const int ns = (sp.m + ROUTE_SLAB - 1) / ROUTE_SLAB;
+  const int c0 = ch * HCOLS;
+
+  // 1. mean over the pooled rows for columns [c0, c0 + HCOLS): waves split the slabs
+  const int col = c0 + lane;
   float sum = 0.f;
   if (col < d) {
     int i = wave;
-    for (; i + 12 < ns; i += 16) {
+    for (; i + 3 * HW < ns; i += 4 * HW) {
       float x[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = partials[(int64_t)(first + i + 4 * r) * d + col];
+      for (int r = 0; r < 4; ++r) x[r] = partials[(int64_t)(first + i + HW * r) * d + col];
 #pragma unroll
       for (int r = 0; r < 4; ++r) sum += x[r];
     }
-    for (; i < ns; i += 4) sum += partials[(int64_t)(first + i) * d + col];
+    for (; i < ns; i += HW) sum += partials[(int64_t)(first + i) * d + col];
   }
   red[wave][lane] = sum;
   __syncthreads();
-  if (wave == 0 && col < d) {
-    const float t = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
-    pooled[(int64_t)b * d + col] = s.m > 0 ? t / (float)s.m : 0.f;
-  }
-}
-
-// z[b, r] = <W1[r, :], pooled[b, :]> for 4 rows r per workgroup.
-__global__ __launch_bounds__(RT) void route_mlp1(const float* __restrict__ pooled,
-                                                 const float* __restrict__ w1, int d, int d_router,
-                                                 float* __restrict__ z) {
-  __shared__ float red[4][4];
-  const int b = blockIdx.x;
-  const int r0 = blockIdx.y * 4;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* h = pooled + (int64_t)b * d;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int c = tid * 4; c < d; c += RT * 4) {  // d is a multiple of 8
-    const float4 hv = *reinterpret_cast<const float4*>(h + c);
+  if (wave == 0) {
+    float t = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (r0 + r < d_router) {
-        const float4 wv = *reinterpret_cast<const float4*>(w1 + (int64_t)(r0 + r) * d + c);
-        acc[r] += wv.x * hv.x + wv.y * hv.y + wv.z * hv.z + wv.w * hv.w;
-      }
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float x = acc[r];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-    if (lane == 0) red[wave][r] = x;
+    for (int w = 0; w < HW; ++w) t += red[w][lane];
+    hbar[lane] = (col < d && sp.m > 0) ? t / (float)sp.m : 0.f;
   }
   __syncthreads();
-  if (tid < 4 && r0 + tid < d_router)
-    z[(int64_t)b * d_router + r0 + tid] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
-}
 
-// logit[b, g] = <W2[g, :], relu(z[b, :])>; mask = logit > threshold.
-__global__ __launch_bounds__(RT) void route_mlp2(const float* __restrict__ z,
-                                                 const float* __restrict__ w2, int d_router,
-                                                 int n_kv_heads, float threshold,
-                                                 float* __restrict__ logits,
-                                                 int32_t* __restrict__ mask) {
-  const int b = blockIdx.x, g = threadIdx.x;
-  if (g >= n_kv_heads) return;
-  const float* zb = z + (int64_t)b * d_router;
-  const float* wg = w2 + (int64_t)g * d_router;
-  float acc = 0.f;
-  for (int r = 0; r < d_router; ++r) acc = fmaf(wg[r], fmaxf(zb[r], 0.f), acc);
-  if (logits) logits[(int64_t)b * n_kv_heads + g] = acc;
-  mask[(int64_t)b * n_kv_heads + g] = acc > threshold ? 1 : 0;
+  // 2. partial z[j] over this strip: 4 threads per W1 row, 16 columns each
+  const int ncol = min(HCOLS, d - c0);
+  for (int j0 = 0; j0 < d_router; j0 += HT / 4) {
+    const int j = j0 + tid / 4, q4 = tid & 3;
+    float acc = 0.f;
+    if (j < d_router) {
+      const float* wr = w1 + (int64_t)j * d + c0;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int cc = q4 * 16 + e;
+        if (cc < ncol) acc = fmaf(wr[cc], hbar[cc], acc);
+      }
+    }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    if (j < d_router && q4 == 0) zpart[((int64_t)b * nch + ch) * ROUTE_MAX_DR + j] = acc;
+  }
+
+  // 3. the last strip of sequence b finishes: z = sum of strips, logits = W2 relu(z)
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) is_last = atomicAdd(&counters[b], 1) == nch - 1;
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();
+  // z[j]: 4 threads per row each sum a quarter of the strips in order, then the quarters
+  __shared__ float zq[4][ROUTE_MAX_DR];
+  {
+    const int q4 = tid & 3, per = (nch + 3) / 4;
+    for (int j = tid / 4; j < d_router; j += HT / 4) {
+      float z = 0.f;
+      const int c1 = min(nch, (q4 + 1) * per);
+      for (int cstrip = q4 * per; cstrip < c1; ++cstrip)
+        z += __hip_atomic_load(&zpart[((int64_t)b * nch + cstrip) * ROUTE_MAX_DR + j],
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      zq[q4][j] = z;
+    }
+  }
+  __syncthreads();
+  for (int j = tid; j < d_router; j += HT) zs[j] = fmaxf(((zq[0][j] + zq[1][j]) + zq[2][j]) + zq[3][j], 0.f);
+  __syncthreads();
+  for (int gh = tid; gh < n_kv_heads; gh += HT) {
+    const float* wg = w2 + (int64_t)gh * d_router;
+    float acc = 0.f;
+    for (int r = 0; r < d_router; ++r) acc = fmaf(wg[r], zs[r], acc);
+    if (logits) logits[(int64_t)b * n_kv_heads + gh] = acc;
+    mask[(int64_t)b * n_kv_heads + gh] = acc > threshold ? 1 : 0;
+  }
 }
 
 }  // namespace
@@ -213,24 +236,17 @@ hipError_t launch_route(const void* hidden, int hidden_dtype, const int32_t* cu_
                         int64_t total_tokens, int d_model, int pool_head, int pool_tail,
                         const float* w1, int d_router, const float* w2, int n_kv_heads,
                         float threshold, float* logits_out, int32_t* mask_out, float* partials,
-                        int64_t max_slabs, float* pooled, float* zbuf, hipStream_t stream) {
+                        int64_t max_slabs, float* zpart, int32_t* counters, hipStream_t stream) {
   const int chunks = (d_model + RCOLS - 1) / RCOLS;
-  if (max_slabs > 0) {
-    hipLaunchKernelGGL(route_pool_partial, dim3((unsigned)max_slabs, chunks), dim3(RT), 0, stream,
-                       hidden, hidden_dtype, cu_seqlens, batch, total_tokens, d_model, pool_head,
-                       pool_tail, partials);
-  }
+  // at least one workgroup: block (0, 0) also clears the completion counters
+  hipLaunchKernelGGL(route_pool_partial, dim3((unsigned)(max_slabs > 0 ? max_slabs : 1), chunks),
+                     dim3(RT), 0, stream, hidden, hidden_dtype, cu_seqlens, batch, total_tokens,
+                     d_model, pool_head, pool_tail, partials, counters);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(route_pool_finish, dim3(batch, (d_model + FIN_COLS - 1) / FIN_COLS), dim3(RT),
-                     0, stream, partials, cu_seqlens, batch, total_tokens, d_model, pool_head,
-                     pool_tail, pooled);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(route_mlp1, dim3(batch, (d_router + 3) / 4), dim3(RT), 0, stream, pooled, w1,
-                     d_model, d_router, zbuf);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(route_mlp2, dim3(batch), dim3(RT), 0, stream, zbuf, w2, d_router, n_kv_heads,
-                     threshold, logits_out, mask_out);
+  hipLaunchKernelGGL(route_head, dim3(batch, (d_model + HCOLS - 1) / HCOLS), dim3(HT), 0, stream,
+                     partials, cu_seqlens, batch, total_tokens, d_model, pool_head, pool_tail, w1,
+                     d_router, w2, n_kv_heads, threshold, zpart, counters, logits_out, mask_out);
   return hipGetLastError();
 }
 
