@@ -36,7 +36,8 @@ def parse():
     p.add_argument("--no-scaling", action="store_true",
                    help="skip the streaming-head scaling sweeps (length and window)")
     p.add_argument("--copy-probe", action="store_true",
-                   help="run one plain 1 GiB device-to-device copy first (calibrates HBM byte counters)")
+                   help="run one plain elementwise kernel first that reads 1 GiB and writes 1 GiB "
+                        "(calibrates the HBM byte counters)")
     return p.parse_args()
 
 
@@ -102,10 +103,11 @@ def main():
             ev[2].record(stream)
 
     if args.copy_probe:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        # one streaming elementwise kernel (not the runtime's blit kernel): 1 GiB in, 1 GiB out
+        src = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
 

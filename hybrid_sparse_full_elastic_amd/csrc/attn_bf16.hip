@@ -29,8 +29,13 @@
 //    land.  Rows past the sequence end read as zero through the buffer descriptor's range.
 //    Tiles are unpadded with XOR swizzles of the 16-byte chunks chosen so the K row reads
 //    and the transposing V reads are free of LDS bank conflicts.
-//  * Per tile step j: Q.K^T of tile j+1, exp2 of tile j, P.V of tile j, then the mask and
-//    maximum of tile j+1; one barrier per step.
+//  * Per tile step j, two instruction regions fenced with sched_barrier so the issue order is
+//    the written one: the Q.K^T MFMAs of tile j+1 with the exp2 / bf16 packing / row sums of
+//    tile j between them (K fragments read three MFMAs ahead), then the P.V MFMAs of tile j
+//    with the transposing V reads (two ahead) and the maximum of tile j+1 between them.  A
+//    wave keeps its MFMA pipe fed while its own softmax work issues beside it, and the two
+//    waves sharing a SIMD fill each other's gaps.  The mask of an edge tile sits between the
+//    regions; one barrier per step.
 #include "elastic_internal.hpp"
 
 namespace elastic {
@@ -286,44 +291,90 @@ __device__ __forceinline__ void attn_item(
       pending = false;
     }
     const bool has_next = kt_n1 >= 0;
-    qk(kslot + sj1 * SLOT, sn);
+    // Region 1: Q.K^T of tile j+1 (NQK MFMAs; K fragments read three ahead) with the exp2,
+    // bf16 packing and row sums of tile j placed between them.
+    constexpr int NQK = 2 * DC, NPV = 4 * DB;
+    constexpr int PPM = 16 / NQK;  // weight pairs per Q.K^T MFMA
     bf16x8 pop[2][2];
-    const float nm = -m_sc;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        pop[kb][e >> 3][e & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[kb][e], c, nm));
-    // row sum of the bf16 weights the P.V product actually uses, two per v_dot2
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float ls[4] = {0.f, 0.f, 0.f, 0.f};
+    {
+      const uint16_t* ks = kslot + sj1 * SLOT;
+      const float nm = -m_sc;
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+      const f32x16 zero = {};
+      bf16x8 a[NQK];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int i = 0; i < 3; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(ks + (i & 1) * 32 * D + k_roff[i >> 1]);
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
+      for (int i = 0; i < NQK; ++i) {
+        if (i + 3 < NQK)
+          a[i + 3] = *reinterpret_cast<const bf16x8*>(ks + ((i + 3) & 1) * 32 * D + k_roff[(i + 3) >> 1]);
+        sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], qreg[i >> 1], i < 2 ? zero : sn[i & 1], 0, 0, 0);
 #pragma unroll
-        for (int pr = 0; pr < 4; ++pr)
-          ls[pr] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pop[kb][cc][2 * pr], pop[kb][cc][2 * pr + 1]},
-                                                   ones, ls[pr], false);
-    // V^T operands: ds_read_b64_tr_b16 gives lane (16-lane group, index l) the values
-    // V[key_i][dbase + l] for the four keys its group's source lanes point at
-    const uint16_t* vs = vslot + sj * SLOT;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const uint16_t* src = vs + v_roff[db] + (kb * 32 + cc * 16) * D;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 8 * D));
-          const bf16x8 a = __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[kb][cc], oacc[db], 0, 0, 0);
+        for (int u = 0; u < PPM; ++u) {
+          const int pair = i * PPM + u;
+          const int kb = pair >> 3, e = (pair & 7) * 2;
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], c, nm));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][e + 1], c, nm));
+          const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+          pop[kb][e >> 3][e & 7] = pp[0];
+          pop[kb][e >> 3][(e & 7) + 1] = pp[1];
+          ls[pair & 3] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls[pair & 3], false);
         }
-    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-    if (has_next) {
-      if (tiles.needs_mask(kt_n1)) apply_mask(sn, kt_n1);
-      update_max(sn);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // keep tile j's weights in this region (no sinking past the mask branch)
+    asm volatile("" ::"v"(pop[0][0]), "v"(pop[0][1]), "v"(pop[1][0]), "v"(pop[1][1]), "v"(ls[0]),
+                 "v"(ls[1]), "v"(ls[2]), "v"(ls[3]));
+    if (has_next && tiles.needs_mask(kt_n1)) apply_mask(sn, kt_n1);
+    // Region 2: P.V of tile j (NPV MFMAs; transposing V reads two fragments ahead) with the
+    // maximum of tile j+1 placed between them.
+    {
+      const uint16_t* vs = vslot + sj * SLOT;
+      bf16x8 av[NPV];
+      auto vread = [&](int i) {
+        const int db = i >> 2, kb = (i >> 1) & 1, cc = i & 1;
+        const uint16_t* src = vs + v_roff[db] + (kb * 32 + cc * 16) * D;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 8 * D));
+        av[i] = __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      };
+      float m0 = 0.f, m1 = 0.f;
+      auto max_step = [&](int st) {  // nine steps: the tile maximum of S_{j+1}, scaled
+        if (st == 0) {
+          m0 = max3f(sn[0][0], sn[1][0], sn[0][1]);
+          m1 = max3f(sn[1][1], sn[0][2], sn[1][2]);
+        } else if (st < 7) {
+          const int e = 2 * st + 1;
+          m0 = max3f(m0, sn[0][e], sn[1][e]);
+          m1 = max3f(m1, sn[0][e + 1], sn[1][e + 1]);
+        } else if (st == 7) {
+          m0 = max3f(m0, m1, max3f(sn[0][15], sn[1][15], m0));
+        } else {
+          m0 = half_max(m0) * c;
+        }
+      };
+      vread(0);
+      vread(1);
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        if (i + 2 < NPV) vread(i + 2);
+        const int db = i >> 2, kb = (i >> 1) & 1, cc = i & 1;
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], pop[kb][cc], oacc[db], 0, 0, 0);
+        if (i < 9) max_step(i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int st = NPV; st < 9; ++st) max_step(st);
+      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      if (has_next && __builtin_amdgcn_ballot_w64(m0 > m_sc + SLACK) != 0) {
+        const float mn = fmaxf(m_sc, m0);
+        alpha = __builtin_amdgcn_exp2f(m_sc - mn);
+        m_sc = mn;
+        pending = true;
+      }
     }
     const int kt_n4 = kt_n3 >= 0 ? tiles.next(kt_n3 + 1) : -1;
     // this step's DMA may stay in flight; the previous step's (K_{j+2}, V_{j+1}) must land
