@@ -36,6 +36,9 @@
 //    wave keeps its MFMA pipe fed while its own softmax work issues beside it, and the two
 //    waves sharing a SIMD fill each other's gaps.  The mask of an edge tile sits between the
 //    regions; one barrier per step.
+//  * Epilogue: each wave stages its 32 normalised rows in the idle tile slots (same swizzle)
+//    and writes whole O rows with 16-byte stores, so the G heads of a token leave as one
+//    contiguous run instead of scattered 8-byte pieces.
 #include "elastic_internal.hpp"
 
 namespace elastic {
@@ -107,6 +110,7 @@ __device__ __forceinline__ void attn_item(
   constexpr int CPR = D / 8;          // 16-byte chunks per tile row
   constexpr int CPT = BK * CPR / NT;  // DMA chunks per thread per tile and operand
   static_assert(CPT >= 1 && CPT * NT == BK * CPR, "tile split");
+  static_assert(NW * 32 * D * 2 <= sizeof(LdsTiles<D>), "O staging fits in the tile slots");
   constexpr float SLACK = 8.0f;       // lazy rescale threshold (log2 units)
   constexpr int SLOT = BK * D;        // elements per LDS slot
 
@@ -398,11 +402,11 @@ __device__ __forceinline__ void attn_item(
     if (kt_cur < 0) break;
   }
 
-  // ---- epilogue: normalise, store bf16 O (and the natural-log LSE)
+  // ---- epilogue: normalise, stage the wave's 32 rows in LDS (every wave passed the last
+  // barrier, so the K/V slots are idle), then write whole O rows with 16-byte stores
   const float lt = half_sum(l_run);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-  if (!qvalid) return;
-  uint16_t* dst = o + ((seq0 + qi) * Hq + qhead) * (int64_t)D;
+  uint16_t* stage = reinterpret_cast<uint16_t*>(&lds) + wave * 32 * D;  // 32 rows x D, swizzled
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -410,9 +414,22 @@ __device__ __forceinline__ void attn_item(
       bf16x4 w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[db][ig * 4 + e] * inv);
-      *reinterpret_cast<u32x2*>(dst + db * 32 + ig * 8 + half * 4) = __builtin_bit_cast(u32x2, w);
+      const int chunk = db * 4 + ig;  // d = chunk * 8 + half * 4 + e
+      *reinterpret_cast<u32x2*>(stage + l32 * D + ((chunk ^ k_swizzle<D>(l32)) * 8) + half * 4) =
+          __builtin_bit_cast(u32x2, w);
     }
-  if (lse != nullptr && half == 0)
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave reads back its own rows
+  constexpr int RPI = 64 / CPR;                        // rows per store instruction
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int rr = i * RPI + lane / CPR, cc = lane % CPR;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(stage + rr * D + ((cc ^ k_swizzle<D>(rr)) * 8));
+    const int row = wave * 32 + rr;
+    const int rt = row / G;
+    if (rt < BT && t0 + rt <= t1)
+      *reinterpret_cast<u32x4*>(o + ((seq0 + t0 + rt) * Hq + g * G + (row - rt * G)) * (int64_t)D + cc * 8) = val;
+  }
+  if (lse != nullptr && half == 0 && qvalid)
     lse[(int64_t)qhead * total_tokens + seq0 + qi] = (m_sc + __log2f(lt)) * LN2;
 }
 
