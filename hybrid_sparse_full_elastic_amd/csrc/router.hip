@@ -156,19 +156,32 @@ __global__ __launch_bounds__(HT) void route_head(
   const int ns = (sp.m + ROUTE_SLAB - 1) / ROUTE_SLAB;
   const int c0 = ch * HCOLS;
 
-  // 1. mean over the pooled rows for columns [c0, c0 + HCOLS): waves split the slabs
+  // W1 strip of this workgroup, fetched first so its latency overlaps the partial sums:
+  // 4 threads per W1 row, 16 columns each
+  const int ncol = min(HCOLS, d - c0);
+  const int jrow = tid / 4, q4 = tid & 3;
+  float w1r[16];
+  if (jrow < d_router) {
+    const float* wr = w1 + (int64_t)jrow * d + c0 + q4 * 16;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) w1r[e] = (q4 * 16 + e < ncol) ? wr[e] : 0.f;
+  }
+
+  // 1. mean over the pooled rows for columns [c0, c0 + HCOLS): waves split the slabs, up to
+  //    16 slab rows in flight per lane, each wave summing its slabs in increasing order
   const int col = c0 + lane;
   float sum = 0.f;
   if (col < d) {
-    int i = wave;
-    for (; i + 3 * HW < ns; i += 4 * HW) {
-      float x[4];
+    for (int i0 = wave; i0 < ns; i0 += 16 * HW) {
+      float x[16];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = partials[(int64_t)(first + i + HW * r) * d + col];
+      for (int r = 0; r < 16; ++r) {
+        const int i = i0 + HW * r;
+        x[r] = i < ns ? partials[(int64_t)(first + i) * d + col] : 0.f;
+      }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sum += x[r];
+      for (int r = 0; r < 16; ++r) sum += x[r];
     }
-    for (; i < ns; i += HW) sum += partials[(int64_t)(first + i) * d + col];
   }
   red[wave][lane] = sum;
   __syncthreads();
@@ -180,22 +193,17 @@ __global__ __launch_bounds__(HT) void route_head(
   }
   __syncthreads();
 
-  // 2. partial z[j] over this strip: 4 threads per W1 row, 16 columns each
-  const int ncol = min(HCOLS, d - c0);
-  for (int j0 = 0; j0 < d_router; j0 += HT / 4) {
-    const int j = j0 + tid / 4, q4 = tid & 3;
+  // 2. partial z[j] over this strip
+  static_assert(HT / 4 >= ROUTE_MAX_DR, "one pass over the W1 rows");
+  {
     float acc = 0.f;
-    if (j < d_router) {
-      const float* wr = w1 + (int64_t)j * d + c0;
+    if (jrow < d_router) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int cc = q4 * 16 + e;
-        if (cc < ncol) acc = fmaf(wr[cc], hbar[cc], acc);
-      }
+      for (int e = 0; e < 16; ++e) acc = fmaf(w1r[e], hbar[q4 * 16 + e], acc);
     }
     acc += __shfl_xor(acc, 1);
     acc += __shfl_xor(acc, 2);
-    if (j < d_router && q4 == 0) zpart[((int64_t)b * nch + ch) * ROUTE_MAX_DR + j] = acc;
+    if (jrow < d_router && q4 == 0) zpart[((int64_t)b * nch + ch) * ROUTE_MAX_DR + jrow] = acc;
   }
 
   // 3. the last strip of sequence b finishes: z = sum of strips, logits = W2 relu(z)
@@ -212,9 +220,16 @@ __global__ __launch_bounds__(HT) void route_head(
     for (int j = tid / 4; j < d_router; j += HT / 4) {
       float z = 0.f;
       const int c1 = min(nch, (q4 + 1) * per);
-      for (int cstrip = q4 * per; cstrip < c1; ++cstrip)
-        z += __hip_atomic_load(&zpart[((int64_t)b * nch + cstrip) * ROUTE_MAX_DR + j],
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int cs0 = q4 * per; cs0 < c1; cs0 += 16) {
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          x[r] = cs0 + r < c1 ? __hip_atomic_load(&zpart[((int64_t)b * nch + cs0 + r) * ROUTE_MAX_DR + j],
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                              : 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) z += x[r];
+      }
       zq[q4][j] = z;
     }
   }
