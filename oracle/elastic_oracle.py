@@ -35,6 +35,19 @@ What is computed (readings of points the summary leaves open are marked READING)
 * Counters: entries (allowed (query, key) pairs over all query heads), effective
   FLOPs = 4*D*entries, model sparsity ratio (fraction of sparse heads) and effective
   sparsity (section 2 "Sparsity Ratio Computation").
+* Deployment forms (appendix D.1 "Sparse Inference": block-sparse streaming with block
+  64 and 128 sink tokens, prefill in chunks of 16,384 queries):
+    attention_kv     queries at absolute positions attend a range of keys at absolute
+                     positions; the allowed sets above are evaluated on absolute positions
+                     and restricted to the keys present.  A row that sees no key has
+                     o = 0 and lse = -inf.
+    lse_merge        the plain identity for softmax attention over two disjoint key sets:
+                     lse = log(e^a + e^b),  o = e^(a - lse) o_a + e^(b - lse) o_b.
+    chunked_prefill  each query chunk attends every key up to its own end (the queries
+                     are the last positions of the keys), chunk results concatenated.
+    block_streaming  READING: the block-granular form of sink + window streaming is the
+                     block pattern with block 64, ceil(sink / 64) sink blocks, a window of
+                     window / 64 blocks that includes the query's own block, and no stride.
 """
 from __future__ import annotations
 
@@ -283,3 +296,105 @@ def attention(q, k, v, cu_seqlens, head_mask, sparse, scale: Optional[float] = N
         with limit, ThreadPoolExecutor(workers) as ex:
             list(ex.map(run, tasks))
     return o, lse
+
+
+# ----------------------------------------------------------------------------- deployment forms
+def block_streaming(sink_tokens: int = 128, window_tokens: int = 1024, block: int = 64) -> dict:
+    """Block-granular streaming pattern (appendix D.1: block 64, 128 sink tokens)."""
+    if window_tokens % block or window_tokens < block:
+        raise ValueError("window must be a positive multiple of the block size")
+    return {"kind": "block", "block": block, "sink_blocks": -(-sink_tokens // block),
+            "local_blocks": window_tokens // block - 1, "stride_blocks": 0}
+
+
+def _attend_block_abs(Q, K, V, pi, pj, full, sparse, scale):
+    """Query rows at absolute positions ``pi`` over keys at absolute positions ``pj``."""
+    A = allowed(pi[:, None], pj[None, :], full, sparse)
+    cols = np.nonzero(A.any(axis=0))[0]
+    o = np.zeros((len(pi), V.shape[1]))
+    lse = np.full(len(pi), -np.inf)
+    if len(cols) == 0:
+        return o, lse
+    A = A[:, cols]
+    s = scale * (Q @ K[cols].T)
+    s = np.where(A, s, -np.inf)
+    has = A.any(axis=1)
+    m = np.where(has, s.max(axis=1), 0.0)[:, None]
+    p = np.exp(s - m)                      # exp(-inf) = 0 for disallowed keys
+    denom = p.sum(axis=1, keepdims=True)
+    o[has] = (p[has] @ V[cols]) / denom[has]
+    lse[has] = m[has, 0] + np.log(denom[has, 0])
+    return o, lse
+
+
+def attention_kv(q, k, v, cu_q, cu_k, head_mask, sparse, scale: Optional[float] = None,
+                 q_pos=None, k_pos: int = 0, heads=None, block_rows: int = 64):
+    """Queries of sequence b (rows cu_q[b]..cu_q[b+1]) sit at absolute positions
+    q_pos[b] + t; its keys (rows cu_k[b]..cu_k[b+1] of k/v) at k_pos + j.  ``q_pos`` None
+    means the queries are the last positions of the keys (q_pos[b] = k_pos + n_k - n_q).
+    Returns o [Tq, len(heads), D] and lse [len(heads), Tq] (natural log)."""
+    Qa, Ka, Va = as_f64(q), as_f64(k), as_f64(v)
+    Tq, Hq, D = Qa.shape
+    Hkv = Ka.shape[1]
+    G = Hq // Hkv
+    scale = D ** -0.5 if scale is None or scale <= 0 else float(scale)
+    cq = _seq_bounds(cu_q, Tq)
+    ck = _seq_bounds(cu_k, Ka.shape[0])
+    B = len(cq) - 1
+    modes = head_modes(head_mask, B, Hkv)
+    heads = list(range(Hq)) if heads is None else list(heads)
+    o = np.zeros((Tq, len(heads), Va.shape[2]))
+    lse = np.full((len(heads), Tq), -np.inf)
+    for b in range(B):
+        nq, nk = int(cq[b + 1] - cq[b]), int(ck[b + 1] - ck[b])
+        if nq == 0:
+            continue
+        qp = (k_pos + nk - nq) if q_pos is None else int(np.asarray(q_pos).reshape(-1)[b])
+        pj = k_pos + np.arange(nk)
+        for hi, h in enumerate(heads):
+            g = h // G
+            K = Ka[ck[b]:ck[b + 1], g, :]
+            V = Va[ck[b]:ck[b + 1], g, :]
+            for r0 in range(0, nq, block_rows):
+                t = np.arange(r0, min(nq, r0 + block_rows))
+                ob, lb = _attend_block_abs(Qa[cq[b] + t, h, :], K, V, qp + t, pj,
+                                           bool(modes[b, g]), sparse, scale)
+                o[cq[b] + t, hi, :] = ob
+                lse[hi, cq[b] + t] = lb
+    return o, lse
+
+
+def lse_merge(o_a, lse_a, o_b, lse_b):
+    """Combine attention over two disjoint key sets: o [rows, heads, D], lse [heads, rows]."""
+    a = np.asarray(lse_a, dtype=np.float64)
+    b = np.asarray(lse_b, dtype=np.float64)
+    lse = np.logaddexp(a, b)                # -inf when both are -inf
+    fin = np.isfinite(lse)
+    safe = np.where(fin, lse, 0.0)
+    wa = np.where(fin, np.exp(np.where(fin, a, 0.0) - safe), 0.0)
+    wb = np.where(fin, np.exp(np.where(fin, b, 0.0) - safe), 0.0)
+    o = wa.T[:, :, None] * as_f64(o_a) + wb.T[:, :, None] * as_f64(o_b)
+    return o, lse
+
+
+def chunked_prefill(q, k, v, cu_seqlens, head_mask, sparse, chunk: int,
+                    scale: Optional[float] = None, heads=None):
+    """Prefill in query chunks: chunk c of sequence b attends its keys up to the chunk's end."""
+    Qa = as_f64(q)
+    T = Qa.shape[0]
+    cu = _seq_bounds(cu_seqlens, T)
+    Hq = Qa.shape[1] if heads is None else len(heads)
+    o = np.zeros((T, Hq, as_f64(v).shape[2]))
+    lse = np.full((Hq, T), -np.inf)
+    mask = None if head_mask is None else np.asarray(head_mask).reshape(len(cu) - 1, -1)
+    for b in range(len(cu) - 1):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        for c0 in range(lo, hi, chunk):
+            c1 = min(hi, c0 + chunk)
+            ob, lb = attention_kv(q[c0:c1], k[lo:c1], v[lo:c1], None, None,
+                                  None if mask is None else mask[b:b + 1], sparse, scale,
+                                  heads=heads)
+            o[c0:c1] = ob
+            lse[:, c0:c1] = lb
+    return o, lse
+
