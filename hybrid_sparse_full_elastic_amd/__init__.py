@@ -6,6 +6,6 @@ hybrid-head attention) runs in the HIP kernels of ``libelastic.so`` behind the C
 if the library is missing, importing this package raises.
 """
 from ._binding import (  # noqa: F401
-    ABI_VERSION, ElasticError, LIB_PATH, SparseCfg, attn_entries, attn_prefill,
-    attn_workspace_size, lib, route, route_workspace_size, sparse_cfg,
+    ABI_VERSION, ElasticError, LIB_PATH, SparseCfg, attn_entries, attn_prefill, attn_prefill_kv,
+    attn_workspace_size, lib, lse_merge, route, route_workspace_size, sparse_cfg,
 )

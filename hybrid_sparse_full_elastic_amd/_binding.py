@@ -10,7 +10,7 @@ import torch
 # ELASTIC_LIB selects another build of the same library (e.g. a tuning variant).
 LIB_PATH = os.environ.get("ELASTIC_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                          "libelastic.so")
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
 BF16, FP32 = 0, 1
@@ -53,6 +53,12 @@ def _load():
     L.elastic_attn_prefill.restype = C.c_int
     L.elastic_attn_prefill.argtypes = [vp, vp, vp, vp, i32, vp, i32, i64, i32, i32, i32, i32, f32,
                                        vp, C.POINTER(SparseCfg), vp, vp, sz, vp]
+    L.elastic_attn_prefill_kv.restype = C.c_int
+    L.elastic_attn_prefill_kv.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, i64, i64, i32, i32, i32,
+                                          i32, i32, i32, i32, f32, vp, C.POINTER(SparseCfg), vp, vp,
+                                          sz, vp]
+    L.elastic_lse_merge.restype = C.c_int
+    L.elastic_lse_merge.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, vp]
     L.elastic_attn_entries.restype = C.c_int
     L.elastic_attn_entries.argtypes = [C.POINTER(i32), i32, C.POINTER(i32), i32, i32,
                                        C.POINTER(SparseCfg), C.POINTER(i64)]
@@ -190,6 +196,77 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if st != OK:
         raise ElasticError(st, "elastic_attn_prefill")
     return out
+
+
+def attn_prefill_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    cu_seqlens_q: Optional[torch.Tensor] = None,
+                    cu_seqlens_k: Optional[torch.Tensor] = None,
+                    max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
+                    q_pos: int = -1, k_pos: int = 0, head_mask: Optional[torch.Tensor] = None,
+                    sparse=None, softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    stream=None):
+    """Query rows against a separate range of key rows (chunked prefill, key-range splits):
+    returns o [Tq, Hq, D].  q_pos -1 = queries are the last key positions of each sequence."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t)
+        if t.dim() != 3:
+            raise ValueError(f"{name} must be [rows, heads, head_dim]")
+    if q.dtype not in (torch.bfloat16, torch.float32) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share dtype bf16 or fp32")
+    Tq, hq, D = q.shape
+    Tk, hkv = k.shape[0], k.shape[1]
+    if k.shape != (Tk, hkv, D) or v.shape != (Tk, hkv, D):
+        raise ValueError("k and v must be [Tk, n_kv_heads, head_dim] with q's head_dim")
+    B = _seq_args(cu_seqlens_q, Tq)
+    if (cu_seqlens_k is None) != (cu_seqlens_q is None) or (cu_seqlens_k is not None and _seq_args(cu_seqlens_k, Tk) != B):
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both be given, for the same batch")
+    dtype = BF16 if q.dtype == torch.bfloat16 else FP32
+    if out is None:
+        out = torch.empty_like(q)
+    _check_dev("out", out, q.dtype)
+    _check_dev("lse", lse, torch.float32)
+    _check_dev("head_mask", head_mask, torch.int32)
+    need = attn_workspace_size(dtype, B, Tq, hq, hkv, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    cfg = sparse_cfg(sparse)
+    st = lib.elastic_attn_prefill_kv(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), dtype, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, Tq,
+        Tk, int(max_seqlen_q if max_seqlen_q is not None else Tq),
+        int(max_seqlen_k if max_seqlen_k is not None else Tk), int(q_pos), int(k_pos), hq, hkv, D,
+        float(softmax_scale), _ptr(head_mask), C.byref(cfg) if cfg is not None else None, _ptr(lse),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != OK:
+        raise ElasticError(st, "elastic_attn_prefill_kv")
+    return out
+
+
+def lse_merge(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b: torch.Tensor,
+              out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None,
+              stream=None):
+    """Merge two attention results over disjoint key sets; in place when out is o_a."""
+    for name, t in (("o_a", o_a), ("o_b", o_b)):
+        _check_dev(name, t)
+    _check_dev("lse_a", lse_a, torch.float32)
+    _check_dev("lse_b", lse_b, torch.float32)
+    if o_a.dim() != 3 or o_b.shape != o_a.shape or o_b.dtype != o_a.dtype:
+        raise ValueError("o_a and o_b must be matching [rows, heads, head_dim] tensors")
+    rows, heads, D = o_a.shape
+    if lse_a.shape != (heads, rows) or lse_b.shape != (heads, rows):
+        raise ValueError("lse_a and lse_b must be [heads, rows]")
+    if out is None:
+        out = torch.empty_like(o_a)
+    if lse_out is None:
+        lse_out = torch.empty_like(lse_a)
+    _check_dev("out", out, o_a.dtype)
+    _check_dev("lse_out", lse_out, torch.float32)
+    dtype = BF16 if o_a.dtype == torch.bfloat16 else FP32
+    st = lib.elastic_lse_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(out),
+                               _ptr(lse_out), dtype, rows, heads, D, _stream(stream))
+    if st != OK:
+        raise ElasticError(st, "elastic_lse_merge")
+    return out, lse_out
 
 
 def attn_entries(seqlens, head_mask, n_q_heads: int, n_kv_heads: int, sparse=None) -> int:

@@ -102,8 +102,8 @@ template <int D, int MODE>
 __device__ __forceinline__ void attn_item(
     const WorkItem& it, LdsTiles<D>& lds, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
-    float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens, int64_t total_tokens, int Hq,
-    int Hkv, int G, int BT, float scale_log2, const Pattern& pat) {
+    float* __restrict__ lse, const SeqGeom& geo, int Hq, int Hkv, int G, int BT, float scale_log2,
+    const Pattern& pat) {
   constexpr int NW = BF16_NW, BK = BF16_BK, NT = NW * 64;
   constexpr int DC = D / 16;          // 16-wide d chunks of Q.K^T
   constexpr int DB = D / 32;          // 32-row d blocks of O^T
@@ -114,28 +114,32 @@ __device__ __forceinline__ void attn_item(
   constexpr float SLACK = 8.0f;       // lazy rescale threshold (log2 units)
   constexpr int SLOT = BK * D;        // elements per LDS slot
 
-  const int64_t seq0 = cu_seqlens ? cu_seqlens[it.seq] : 0;
-  const int n = cu_seqlens ? cu_seqlens[it.seq + 1] - (int)seq0 : (int)total_tokens;
+  // rows of this sequence: queries at absolute positions sp.qp + t, keys at k_pos + j
+  const SeqSpan sp = seq_span(geo, it.seq);
+  const int64_t seq0 = sp.q0;
+  const int n = sp.nq;
   const int t0 = it.qtile * BT;
   const int t1 = min(t0 + BT, n) - 1;
   const int g = it.group;
-  const KeyTilesT<MODE> tiles(MODE, pat, t0, t1, BK);
+  const int k_end = geo.k_pos + sp.nk;  // one past the last key (absolute)
+  const KeyTilesT<MODE> tiles(MODE, pat, sp.qp + t0, sp.qp + t1, BK, geo.k_pos, k_end);
   const int blk_shift = 31 - __clz(pat.block);  // block sizes are powers of two
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
   const int64_t kv_row = (int64_t)Hkv * D;  // elements between consecutive tokens of k / v
-  const uint16_t* kbase = k + seq0 * kv_row + (int64_t)g * D;
-  const uint16_t* vbase = v + seq0 * kv_row + (int64_t)g * D;
+  const uint16_t* kbase = k + sp.k0 * kv_row + (int64_t)g * D;
+  const uint16_t* vbase = v + sp.k0 * kv_row + (int64_t)g * D;
   const float c = scale_log2;
 
   // ---- this lane's query row: r = token * G + head inside the item
   const int r = wave * 32 + l32;
   const int tl = r / G;
-  const int qi = t0 + tl;
+  const int qi = t0 + tl;          // query row within the sequence
+  const int qabs = sp.qp + qi;     // its absolute position
   const int qhead = g * G + (r - tl * G);
   const bool qvalid = tl < BT && qi <= t1;
-  const int qblk = qi >> blk_shift;
+  const int qblk = qabs >> blk_shift;
   bf16x8 qreg[DC];
   if (qvalid) {
     const u32x4* src = reinterpret_cast<const u32x4*>(q + ((seq0 + qi) * Hq + qhead) * (int64_t)D + half * 8);
@@ -156,10 +160,13 @@ __device__ __forceinline__ void attn_item(
     k_voff[m] = (row * (int)kv_row + (pc ^ k_swizzle<D>(row)) * 8) * 2;
     v_voff[m] = (row * (int)kv_row + (pc ^ v_swizzle<D>(row)) * 8) * 2;
   }
+  // tile kt (absolute) holds key rows [kt * BK - k_pos, +BK) of the sequence; rows past the
+  // key range read as zero through the descriptor's range
   auto tile_rsrc = [&](const uint16_t* base, int kt) {
-    const int rows = min(n - kt * BK, BK);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + (int64_t)kt * BK * kv_row),
-                                             (short)0, rows * (int)kv_row * 2, 0x00020000);
+    const int rows = min(k_end - kt * BK, BK);
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(base + (int64_t)(kt * BK - geo.k_pos) * kv_row), (short)0,
+        rows * (int)kv_row * 2, 0x00020000);
   };
   auto dma = [&](const uint16_t* base, int kt, uint16_t* slot, const int (&voff)[CPT]) {
     const auto rs = tile_rsrc(base, kt);
@@ -203,11 +210,11 @@ __device__ __forceinline__ void attn_item(
 
   // ---- exact masks on edge tiles: allowed(j) = j <= hi && (j < a || j >= b)
   auto apply_mask = [&](f32x16 (&s)[2], int kt) {
-    const int hi = qvalid ? qi : -1;
+    const int hi = qvalid ? min(qabs, k_end - 1) : -1;
     int a = 0, b = 0;
     if (MODE == MODE_STREAM) {
       a = pat.sink;
-      b = qi - pat.window + 1;
+      b = qabs - pat.window + 1;
     } else if (MODE == MODE_BLOCK) {
       const int kblk = (kt * BK) >> blk_shift;  // one key block per tile (block % BK == 0)
       const bool vis = kblk < pat.sink_blocks || qblk - kblk <= pat.local_blocks ||
@@ -252,154 +259,157 @@ __device__ __forceinline__ void attn_item(
   };
 
   // ---- tile schedule: kt_cur = tile j, kt_n1/2/3 = tiles j+1..j+3 (-1 when absent)
+  // An item whose queries see no key of the range (a query chunk placed before its key
+  // range) skips straight to the epilogue and writes O = 0, lse = -inf.
   int kt_cur = tiles.next(0);
-  if (kt_cur < 0) return;  // cannot happen: the diagonal tile is always visited
-  int kt_n1 = tiles.next(kt_cur + 1);
-  int kt_n2 = kt_n1 >= 0 ? tiles.next(kt_n1 + 1) : -1;
-  int kt_n3 = kt_n2 >= 0 ? tiles.next(kt_n2 + 1) : -1;
+  if (kt_cur >= 0) {
+    int kt_n1 = tiles.next(kt_cur + 1);
+    int kt_n2 = kt_n1 >= 0 ? tiles.next(kt_n1 + 1) : -1;
+    int kt_n3 = kt_n2 >= 0 ? tiles.next(kt_n2 + 1) : -1;
 
-  // prologue: K_0..K_2 and V_0, V_1 land; S_0 computed and reduced
-  uint16_t* kslot = &lds.k[0][0];
-  uint16_t* vslot = &lds.v[0][0];
-  dma(kbase, kt_cur, kslot, k_voff);
-  dma(vbase, kt_cur, vslot, v_voff);
-  if (kt_n1 >= 0) {
-    dma(kbase, kt_n1, kslot + SLOT, k_voff);
-    dma(vbase, kt_n1, vslot + SLOT, v_voff);
-  }
-  if (kt_n2 >= 0) dma(kbase, kt_n2, kslot + 2 * SLOT, k_voff);
-  WAIT_VMCNT(0);
-  __syncthreads();
-  f32x16 s0[2], s1[2];
-  qk(kslot, s0);
-  __syncthreads();  // every wave is done with K slot 0 before step 0 refills it
-  if (tiles.needs_mask(kt_cur)) apply_mask(s0, kt_cur);
-  update_max(s0);
-  pending = false;  // O and l are still zero
-  int sj = 0;       // LDS slot of tile j (tile t lives in slot t mod 3)
-
-  // One step on tile j: DMA K_{j+3} and V_{j+2}; S_{j+1} = K_{j+1} Q^T; p_j = exp2(c s_j - m);
-  // O += V_j^T P_j^T; mask and maximum of S_{j+1}; wait for the previous step's DMA; barrier.
-  auto step = [&](f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-    const int sj1 = sj == NSLOT - 1 ? 0 : sj + 1;
-    const int sj2 = sj1 == NSLOT - 1 ? 0 : sj1 + 1;
-    const int n_dma = (kt_n3 >= 0 ? CPT : 0) + (kt_n2 >= 0 ? CPT : 0);
-    if (kt_n3 >= 0) dma(kbase, kt_n3, kslot + sj * SLOT, k_voff);   // slot of K_j, read last step
-    if (kt_n2 >= 0) dma(vbase, kt_n2, vslot + sj2 * SLOT, v_voff);  // slot of V_{j-1}, read last step
-    if (pending) {
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-      pending = false;
+    // prologue: K_0..K_2 and V_0, V_1 land; S_0 computed and reduced
+    uint16_t* kslot = &lds.k[0][0];
+    uint16_t* vslot = &lds.v[0][0];
+    dma(kbase, kt_cur, kslot, k_voff);
+    dma(vbase, kt_cur, vslot, v_voff);
+    if (kt_n1 >= 0) {
+      dma(kbase, kt_n1, kslot + SLOT, k_voff);
+      dma(vbase, kt_n1, vslot + SLOT, v_voff);
     }
-    const bool has_next = kt_n1 >= 0;
-    // Region 1: Q.K^T of tile j+1 (NQK MFMAs; K fragments read three ahead) with the exp2,
-    // bf16 packing and row sums of tile j placed between them.
-    constexpr int NQK = 2 * DC, NPV = 4 * DB;
-    constexpr int PPM = 16 / NQK;  // weight pairs per Q.K^T MFMA
-    bf16x8 pop[2][2];
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
-    {
-      const uint16_t* ks = kslot + sj1 * SLOT;
-      const float nm = -m_sc;
-      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-      const f32x16 zero = {};
-      bf16x8 a[NQK];
+    if (kt_n2 >= 0) dma(kbase, kt_n2, kslot + 2 * SLOT, k_voff);
+    WAIT_VMCNT(0);
+    __syncthreads();
+    f32x16 s0[2], s1[2];
+    qk(kslot, s0);
+    __syncthreads();  // every wave is done with K slot 0 before step 0 refills it
+    if (tiles.needs_mask(kt_cur)) apply_mask(s0, kt_cur);
+    update_max(s0);
+    pending = false;  // O and l are still zero
+    int sj = 0;       // LDS slot of tile j (tile t lives in slot t mod 3)
+
+    // One step on tile j: DMA K_{j+3} and V_{j+2}; S_{j+1} = K_{j+1} Q^T; p_j = exp2(c s_j - m);
+    // O += V_j^T P_j^T; mask and maximum of S_{j+1}; wait for the previous step's DMA; barrier.
+    auto step = [&](f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+      const int sj1 = sj == NSLOT - 1 ? 0 : sj + 1;
+      const int sj2 = sj1 == NSLOT - 1 ? 0 : sj1 + 1;
+      const int n_dma = (kt_n3 >= 0 ? CPT : 0) + (kt_n2 >= 0 ? CPT : 0);
+      if (kt_n3 >= 0) dma(kbase, kt_n3, kslot + sj * SLOT, k_voff);   // slot of K_j, read last step
+      if (kt_n2 >= 0) dma(vbase, kt_n2, vslot + sj2 * SLOT, v_voff);  // slot of V_{j-1}, read last step
+      if (pending) {
+        l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < 3; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(ks + (i & 1) * 32 * D + k_roff[i >> 1]);
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < NQK; ++i) {
-        if (i + 3 < NQK)
-          a[i + 3] = *reinterpret_cast<const bf16x8*>(ks + ((i + 3) & 1) * 32 * D + k_roff[(i + 3) >> 1]);
-        sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], qreg[i >> 1], i < 2 ? zero : sn[i & 1], 0, 0, 0);
+          for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+        pending = false;
+      }
+      const bool has_next = kt_n1 >= 0;
+      // Region 1: Q.K^T of tile j+1 (NQK MFMAs; K fragments read three ahead) with the exp2,
+      // bf16 packing and row sums of tile j placed between them.
+      constexpr int NQK = 2 * DC, NPV = 4 * DB;
+      constexpr int PPM = 16 / NQK;  // weight pairs per Q.K^T MFMA
+      bf16x8 pop[2][2];
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
+      {
+        const uint16_t* ks = kslot + sj1 * SLOT;
+        const float nm = -m_sc;
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        const f32x16 zero = {};
+        bf16x8 a[NQK];
 #pragma unroll
-        for (int u = 0; u < PPM; ++u) {
-          const int pair = i * PPM + u;
-          const int kb = pair >> 3, e = (pair & 7) * 2;
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], c, nm));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][e + 1], c, nm));
-          const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
-          pop[kb][e >> 3][e & 7] = pp[0];
-          pop[kb][e >> 3][(e & 7) + 1] = pp[1];
-          ls[pair & 3] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls[pair & 3], false);
+        for (int i = 0; i < 3; ++i)
+          a[i] = *reinterpret_cast<const bf16x8*>(ks + (i & 1) * 32 * D + k_roff[i >> 1]);
+#pragma unroll
+        for (int i = 0; i < NQK; ++i) {
+          if (i + 3 < NQK)
+            a[i + 3] = *reinterpret_cast<const bf16x8*>(ks + ((i + 3) & 1) * 32 * D + k_roff[(i + 3) >> 1]);
+          sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], qreg[i >> 1], i < 2 ? zero : sn[i & 1], 0, 0, 0);
+#pragma unroll
+          for (int u = 0; u < PPM; ++u) {
+            const int pair = i * PPM + u;
+            const int kb = pair >> 3, e = (pair & 7) * 2;
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], c, nm));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][e + 1], c, nm));
+            const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+            pop[kb][e >> 3][e & 7] = pp[0];
+            pop[kb][e >> 3][(e & 7) + 1] = pp[1];
+            ls[pair & 3] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls[pair & 3], false);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
-    }
-    // keep tile j's weights in this region (no sinking past the mask branch)
-    asm volatile("" ::"v"(pop[0][0]), "v"(pop[0][1]), "v"(pop[1][0]), "v"(pop[1][1]), "v"(ls[0]),
-                 "v"(ls[1]), "v"(ls[2]), "v"(ls[3]));
-    if (has_next && tiles.needs_mask(kt_n1)) apply_mask(sn, kt_n1);
-    // Region 2: P.V of tile j (NPV MFMAs; transposing V reads two fragments ahead) with the
-    // maximum of tile j+1 placed between them.
-    {
-      const uint16_t* vs = vslot + sj * SLOT;
-      bf16x8 av[NPV];
-      auto vread = [&](int i) {
-        const int db = i >> 2, kb = (i >> 1) & 1, cc = i & 1;
-        const uint16_t* src = vs + v_roff[db] + (kb * 32 + cc * 16) * D;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 8 * D));
-        av[i] = __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-      };
-      float m0 = 0.f, m1 = 0.f;
-      auto max_step = [&](int st) {  // nine steps: the tile maximum of S_{j+1}, scaled
-        if (st == 0) {
-          m0 = max3f(sn[0][0], sn[1][0], sn[0][1]);
-          m1 = max3f(sn[1][1], sn[0][2], sn[1][2]);
-        } else if (st < 7) {
-          const int e = 2 * st + 1;
-          m0 = max3f(m0, sn[0][e], sn[1][e]);
-          m1 = max3f(m1, sn[0][e + 1], sn[1][e + 1]);
-        } else if (st == 7) {
-          m0 = max3f(m0, m1, max3f(sn[0][15], sn[1][15], m0));
-        } else {
-          m0 = half_max(m0) * c;
+      // keep tile j's weights in this region (no sinking past the mask branch)
+      asm volatile("" ::"v"(pop[0][0]), "v"(pop[0][1]), "v"(pop[1][0]), "v"(pop[1][1]), "v"(ls[0]),
+                   "v"(ls[1]), "v"(ls[2]), "v"(ls[3]));
+      if (has_next && tiles.needs_mask(kt_n1)) apply_mask(sn, kt_n1);
+      // Region 2: P.V of tile j (NPV MFMAs; transposing V reads two fragments ahead) with the
+      // maximum of tile j+1 placed between them.
+      {
+        const uint16_t* vs = vslot + sj * SLOT;
+        bf16x8 av[NPV];
+        auto vread = [&](int i) {
+          const int db = i >> 2, kb = (i >> 1) & 1, cc = i & 1;
+          const uint16_t* src = vs + v_roff[db] + (kb * 32 + cc * 16) * D;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 8 * D));
+          av[i] = __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        };
+        float m0 = 0.f, m1 = 0.f;
+        auto max_step = [&](int st) {  // nine steps: the tile maximum of S_{j+1}, scaled
+          if (st == 0) {
+            m0 = max3f(sn[0][0], sn[1][0], sn[0][1]);
+            m1 = max3f(sn[1][1], sn[0][2], sn[1][2]);
+          } else if (st < 7) {
+            const int e = 2 * st + 1;
+            m0 = max3f(m0, sn[0][e], sn[1][e]);
+            m1 = max3f(m1, sn[0][e + 1], sn[1][e + 1]);
+          } else if (st == 7) {
+            m0 = max3f(m0, m1, max3f(sn[0][15], sn[1][15], m0));
+          } else {
+            m0 = half_max(m0) * c;
+          }
+        };
+        vread(0);
+        vread(1);
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+          if (i + 2 < NPV) vread(i + 2);
+          const int db = i >> 2, kb = (i >> 1) & 1, cc = i & 1;
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], pop[kb][cc], oacc[db], 0, 0, 0);
+          if (i < 9) max_step(i);
+          __builtin_amdgcn_sched_barrier(0);
         }
-      };
-      vread(0);
-      vread(1);
 #pragma unroll
-      for (int i = 0; i < NPV; ++i) {
-        if (i + 2 < NPV) vread(i + 2);
-        const int db = i >> 2, kb = (i >> 1) & 1, cc = i & 1;
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], pop[kb][cc], oacc[db], 0, 0, 0);
-        if (i < 9) max_step(i);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int st = NPV; st < 9; ++st) max_step(st);
+        l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        if (has_next && __builtin_amdgcn_ballot_w64(m0 > m_sc + SLACK) != 0) {
+          const float mn = fmaxf(m_sc, m0);
+          alpha = __builtin_amdgcn_exp2f(m_sc - mn);
+          m_sc = mn;
+          pending = true;
+        }
       }
-#pragma unroll
-      for (int st = NPV; st < 9; ++st) max_step(st);
-      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-      if (has_next && __builtin_amdgcn_ballot_w64(m0 > m_sc + SLACK) != 0) {
-        const float mn = fmaxf(m_sc, m0);
-        alpha = __builtin_amdgcn_exp2f(m_sc - mn);
-        m_sc = mn;
-        pending = true;
-      }
-    }
-    const int kt_n4 = kt_n3 >= 0 ? tiles.next(kt_n3 + 1) : -1;
-    // this step's DMA may stay in flight; the previous step's (K_{j+2}, V_{j+1}) must land
-    if (n_dma == 2 * CPT) WAIT_VMCNT(2 * CPT);
-    else if (n_dma == CPT) WAIT_VMCNT(CPT);
-    else WAIT_VMCNT(0);
-    // LDS reads of this step done, then the barrier.  (__syncthreads would also wait for the
-    // DMA issued this step, which must stay in flight.)
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    kt_cur = kt_n1;
-    kt_n1 = kt_n2;
-    kt_n2 = kt_n3;
-    kt_n3 = kt_n4;
-    sj = sj1;
-  };
+      const int kt_n4 = kt_n3 >= 0 ? tiles.next(kt_n3 + 1) : -1;
+      // this step's DMA may stay in flight; the previous step's (K_{j+2}, V_{j+1}) must land
+      if (n_dma == 2 * CPT) WAIT_VMCNT(2 * CPT);
+      else if (n_dma == CPT) WAIT_VMCNT(CPT);
+      else WAIT_VMCNT(0);
+      // LDS reads of this step done, then the barrier.  (__syncthreads would also wait for the
+      // DMA issued this step, which must stay in flight.)
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      kt_cur = kt_n1;
+      kt_n1 = kt_n2;
+      kt_n2 = kt_n3;
+      kt_n3 = kt_n4;
+      sj = sj1;
+    };
 
-  while (true) {
-    step(s0, s1);
-    if (kt_cur < 0) break;
-    step(s1, s0);
-    if (kt_cur < 0) break;
+    while (true) {
+      step(s0, s1);
+      if (kt_cur < 0) break;
+      step(s1, s0);
+      if (kt_cur < 0) break;
+    }
   }
 
   // ---- epilogue: normalise, stage the wave's 32 rows in LDS (every wave passed the last
@@ -429,52 +439,49 @@ __device__ __forceinline__ void attn_item(
     if (rt < BT && t0 + rt <= t1)
       *reinterpret_cast<u32x4*>(o + ((seq0 + t0 + rt) * Hq + g * G + (row - rt * G)) * (int64_t)D + cc * 8) = val;
   }
-  if (lse != nullptr && half == 0 && qvalid)
-    lse[(int64_t)qhead * total_tokens + seq0 + qi] = (m_sc + __log2f(lt)) * LN2;
+  if (lse != nullptr && half == 0 && qvalid)  // log of an empty sum is -inf
+    lse[(int64_t)qhead * geo.total_q + seq0 + qi] = (m_sc + __log2f(lt)) * LN2;
 }
 
 template <int D>
 __global__ __launch_bounds__(BF16_NW * 64, 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens,
-    int64_t total_tokens, int Hq, int Hkv, int G, int BT, float scale_log2,
-    const int32_t* __restrict__ head_mask, Pattern pat, const WorkItem* __restrict__ items,
-    const int32_t* __restrict__ n_items) {
+    uint16_t* __restrict__ o, float* __restrict__ lse, SeqGeom geo, int Hq, int Hkv, int G, int BT,
+    float scale_log2, const int32_t* __restrict__ head_mask, Pattern pat,
+    const WorkItem* __restrict__ items, const int32_t* __restrict__ n_items) {
   __shared__ __attribute__((aligned(1024))) LdsTiles<D> lds;
   if ((int)blockIdx.x >= *n_items) return;
   const WorkItem it = items[blockIdx.x];
   const bool full = head_mask == nullptr || head_mask[it.seq * Hkv + it.group] != 0;
   if (full)
-    attn_item<D, MODE_FULL>(it, lds, q, k, v, o, lse, cu_seqlens, total_tokens, Hq, Hkv, G, BT,
+    attn_item<D, MODE_FULL>(it, lds, q, k, v, o, lse, geo, Hq, Hkv, G, BT,
                             scale_log2, pat);
   else if (pat.kind == ELASTIC_SPARSE_STREAMING)
-    attn_item<D, MODE_STREAM>(it, lds, q, k, v, o, lse, cu_seqlens, total_tokens, Hq, Hkv, G, BT,
+    attn_item<D, MODE_STREAM>(it, lds, q, k, v, o, lse, geo, Hq, Hkv, G, BT,
                               scale_log2, pat);
   else
-    attn_item<D, MODE_BLOCK>(it, lds, q, k, v, o, lse, cu_seqlens, total_tokens, Hq, Hkv, G, BT,
+    attn_item<D, MODE_BLOCK>(it, lds, q, k, v, o, lse, geo, Hq, Hkv, G, BT,
                              scale_log2, pat);
 }
 
 }  // namespace
 
 hipError_t launch_attn_bf16(int head_dim, const void* q, const void* k, const void* v, void* o,
-                            float* lse, const int32_t* cu_seqlens, int64_t total_tokens,
-                            int n_q_heads, int n_kv_heads, int BT, float scale,
-                            const int32_t* head_mask, const Pattern& pat, const WorkItem* items,
-                            const int32_t* n_items, int64_t grid, hipStream_t stream) {
+                            float* lse, const SeqGeom& geo, int n_q_heads, int n_kv_heads, int BT,
+                            float scale, const int32_t* head_mask, const Pattern& pat,
+                            const WorkItem* items, const int32_t* n_items, int64_t grid,
+                            hipStream_t stream) {
   const float scale_log2 = scale * 1.4426950408889634f;
   const int G = n_q_heads / n_kv_heads;
   if (grid <= 0) return hipSuccess;
   if (head_dim == 128)
     hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3((unsigned)grid), dim3(BF16_NW * 64), 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
-                       cu_seqlens, total_tokens, n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask,
-                       pat, items, n_items);
+                       geo, n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask, pat, items, n_items);
   else
     hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3((unsigned)grid), dim3(BF16_NW * 64), 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
-                       cu_seqlens, total_tokens, n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask,
-                       pat, items, n_items);
+                       geo, n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask, pat, items, n_items);
   return hipGetLastError();
 }
 

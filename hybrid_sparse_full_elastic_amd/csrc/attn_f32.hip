@@ -17,10 +17,9 @@ constexpr float LN2 = 0.69314718055994530942f;
 template <int D>
 __global__ __launch_bounds__(F32_ROWS, 1) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    float* __restrict__ o, float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens,
-    int64_t total_tokens, int Hq, int Hkv, int G, int BT, float scale_log2,
-    const int32_t* __restrict__ head_mask, Pattern pat, const WorkItem* __restrict__ items,
-    const int32_t* __restrict__ n_items) {
+    float* __restrict__ o, float* __restrict__ lse, SeqGeom geo, int Hq, int Hkv, int G, int BT,
+    float scale_log2, const int32_t* __restrict__ head_mask, Pattern pat,
+    const WorkItem* __restrict__ items, const int32_t* __restrict__ n_items) {
   constexpr int BK = F32_BK, NT = F32_ROWS;
   constexpr int CH = BK * D / 4;  // float4 chunks per tile
   __shared__ __attribute__((aligned(16))) float k_lds[BK * D];
@@ -28,18 +27,22 @@ __global__ __launch_bounds__(F32_ROWS, 1) void attn_f32_kernel(
 
   if ((int)blockIdx.x >= *n_items) return;
   const WorkItem it = items[blockIdx.x];
-  const int64_t seq0 = cu_seqlens ? cu_seqlens[it.seq] : 0;
-  const int n = cu_seqlens ? cu_seqlens[it.seq + 1] - (int)seq0 : (int)total_tokens;
+  // queries at absolute positions sp.qp + t, keys at k_pos + j
+  const SeqSpan sp = seq_span(geo, it.seq);
+  const int64_t seq0 = sp.q0;
+  const int n = sp.nq;
   const int t0 = it.qtile * BT;
   const int t1 = min(t0 + BT, n) - 1;
   const int g = it.group;
   const bool full = head_mask == nullptr || head_mask[it.seq * Hkv + g] != 0;
   const int mode = full ? MODE_FULL : pat.kind;
-  const KeyTiles tiles(mode, pat, t0, t1, BK);
+  const int k_end = geo.k_pos + sp.nk;
+  const KeyTiles tiles(mode, pat, sp.qp + t0, sp.qp + t1, BK, geo.k_pos, k_end);
 
   const int tid = threadIdx.x;
   const int tl = tid / G, hh = tid - (tid / G) * G;
   const int qi = t0 + tl;
+  const int qabs = sp.qp + qi;
   const int head = g * G + hh;
   const bool valid = tl < BT && qi <= t1;
   const int64_t kv_row = (int64_t)Hkv * D;
@@ -64,11 +67,12 @@ __global__ __launch_bounds__(F32_ROWS, 1) void attn_f32_kernel(
     __syncthreads();  // previous tile fully consumed
     for (int c = tid; c < CH; c += NT) {
       const int row = c / (D / 4), c4 = c % (D / 4);
-      const int key = kt * BK + row;
+      const int key = kt * BK + row;  // absolute; row key - k_pos of the sequence's keys
       float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
-      if (key < n) {
-        kx = *reinterpret_cast<const float4*>(k + (seq0 + key) * kv_row + (int64_t)g * D + c4 * 4);
-        vx = *reinterpret_cast<const float4*>(v + (seq0 + key) * kv_row + (int64_t)g * D + c4 * 4);
+      if (key < k_end) {
+        const int64_t kr = sp.k0 + (key - geo.k_pos);
+        kx = *reinterpret_cast<const float4*>(k + kr * kv_row + (int64_t)g * D + c4 * 4);
+        vx = *reinterpret_cast<const float4*>(v + kr * kv_row + (int64_t)g * D + c4 * 4);
       }
       *reinterpret_cast<float4*>(&k_lds[row * D + c4 * 4]) = kx;
       *reinterpret_cast<float4*>(&v_lds[row * D + c4 * 4]) = vx;
@@ -84,7 +88,8 @@ __global__ __launch_bounds__(F32_ROWS, 1) void attn_f32_kernel(
 #pragma unroll
       for (int d = 0; d < D; ++d) dot = fmaf(qr[d], k_lds[j * D + d], dot);
       float x = dot * scale_log2;
-      if (masked && (!valid || !key_allowed(mode, pat, qi, kt * BK + j))) x = -__builtin_huge_valf();
+      const int kj = kt * BK + j;
+      if (masked && (!valid || kj >= k_end || !key_allowed(mode, pat, qabs, kj))) x = -__builtin_huge_valf();
       s[j] = x;
       mt = fmaxf(mt, x);
     }
@@ -109,29 +114,28 @@ __global__ __launch_bounds__(F32_ROWS, 1) void attn_f32_kernel(
 #pragma unroll
   for (int c = 0; c < D / 4; ++c)
     dst[c] = make_float4(acc[4 * c] * inv, acc[4 * c + 1] * inv, acc[4 * c + 2] * inv, acc[4 * c + 3] * inv);
-  if (lse != nullptr) lse[(int64_t)head * total_tokens + seq0 + qi] = (m_run + __log2f(l_run)) * LN2;
+  if (lse != nullptr)  // log of an empty sum is -inf
+    lse[(int64_t)head * geo.total_q + seq0 + qi] = (m_run + __log2f(l_run)) * LN2;
 }
 
 }  // namespace
 
 hipError_t launch_attn_f32(int head_dim, const void* q, const void* k, const void* v, void* o,
-                           float* lse, const int32_t* cu_seqlens, int64_t total_tokens,
-                           int n_q_heads, int n_kv_heads, int BT, float scale,
-                           const int32_t* head_mask, const Pattern& pat, const WorkItem* items,
-                           const int32_t* n_items, int64_t grid, hipStream_t stream) {
+                           float* lse, const SeqGeom& geo, int n_q_heads, int n_kv_heads, int BT,
+                           float scale, const int32_t* head_mask, const Pattern& pat,
+                           const WorkItem* items, const int32_t* n_items, int64_t grid,
+                           hipStream_t stream) {
   const float scale_log2 = scale * 1.4426950408889634f;
   const int G = n_q_heads / n_kv_heads;
   if (grid <= 0) return hipSuccess;
   if (head_dim == 128) {
     hipLaunchKernelGGL(attn_f32_kernel<128>, dim3((unsigned)grid), dim3(F32_ROWS), 0, stream,
-                       (const float*)q, (const float*)k, (const float*)v, (float*)o, lse, cu_seqlens,
-                       total_tokens, n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask, pat,
-                       items, n_items);
+                       (const float*)q, (const float*)k, (const float*)v, (float*)o, lse, geo,
+                       n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask, pat, items, n_items);
   } else {
     hipLaunchKernelGGL(attn_f32_kernel<64>, dim3((unsigned)grid), dim3(F32_ROWS), 0, stream,
-                       (const float*)q, (const float*)k, (const float*)v, (float*)o, lse, cu_seqlens,
-                       total_tokens, n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask, pat,
-                       items, n_items);
+                       (const float*)q, (const float*)k, (const float*)v, (float*)o, lse, geo,
+                       n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask, pat, items, n_items);
   }
   return hipGetLastError();
 }

@@ -183,53 +183,116 @@ size_t elastic_attn_workspace_size(int32_t dtype, int32_t batch, int64_t total_t
   return attn_layout(attn_max_items(dtype, batch, total_tokens, n_q_heads, n_kv_heads), batch).total;
 }
 
-int elastic_attn_prefill(const void* q, const void* k, const void* v, void* o, int32_t dtype,
-                         const int32_t* cu_seqlens, int32_t batch, int64_t total_tokens,
-                         int32_t max_seqlen, int32_t n_q_heads, int32_t n_kv_heads,
-                         int32_t head_dim, float softmax_scale, const int32_t* head_mask,
-                         const elastic_sparse_cfg* sparse, float* lse_out, void* workspace,
-                         size_t workspace_bytes, void* stream) {
-  if (batch < 1 || total_tokens < 0 || total_tokens > INT32_MAX || max_seqlen < 0)
+}  // extern "C"
+
+namespace {
+
+// Shared body of the two attention entry points: validation, then scheduler + attention.
+int attn_call(const char* who, const void* q, const void* k, const void* v, void* o, int32_t dtype,
+              const int32_t* cu_q, const int32_t* cu_k, int32_t batch, int64_t total_q,
+              int64_t total_k, int32_t max_q, int32_t max_k, int32_t q_pos, int32_t k_pos,
+              int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float softmax_scale,
+              const int32_t* head_mask, const elastic_sparse_cfg* sparse, float* lse_out,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch < 1 || total_q < 0 || total_q > INT32_MAX || total_k < 0 || total_k > INT32_MAX ||
+      max_q < 0 || max_k < 0)
     return ELASTIC_EINVAL;
-  if (total_tokens > 0 && (q == nullptr || k == nullptr || v == nullptr || o == nullptr))
+  if (total_q > 0 && (q == nullptr || o == nullptr)) return ELASTIC_EINVAL;
+  if (total_k > 0 && (k == nullptr || v == nullptr)) return ELASTIC_EINVAL;
+  if ((cu_q == nullptr || cu_k == nullptr) && batch != 1) return ELASTIC_EINVAL;
+  if (q_pos < -1 || k_pos < 0 || k_pos % 64 != 0) return ELASTIC_EINVAL;
+  // absolute positions stay within int32: keys up to k_pos + max_k, queries up to q_pos + max_q
+  if ((int64_t)k_pos + max_k > INT32_MAX || (q_pos >= 0 && (int64_t)q_pos + max_q > INT32_MAX))
     return ELASTIC_EINVAL;
-  if (cu_seqlens == nullptr && batch != 1) return ELASTIC_EINVAL;
   if (n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads != 0) return ELASTIC_EINVAL;
   if (head_mask != nullptr && sparse == nullptr) return ELASTIC_EINVAL;
   if (sparse != nullptr) {
     const int st = check_pattern(sparse);
     if (st != ELASTIC_OK) return st;
+    if (sparse->kind == ELASTIC_SPARSE_BLOCK && k_pos % sparse->block_size != 0) return ELASTIC_EINVAL;
   }
   if (dtype != ELASTIC_BF16 && dtype != ELASTIC_FP32) return ELASTIC_EUNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return ELASTIC_EUNSUPPORTED;
   if (n_q_heads / n_kv_heads > attn_rows_per_item(dtype)) return ELASTIC_EUNSUPPORTED;
-  const int64_t max_items = attn_max_items(dtype, batch, total_tokens, n_q_heads, n_kv_heads);
+  const int64_t max_items = attn_max_items(dtype, batch, total_q, n_q_heads, n_kv_heads);
   if (max_items > INT32_MAX) return ELASTIC_EUNSUPPORTED;
   const AttnWorkspace lay = attn_layout(max_items, batch);
   if (workspace == nullptr || workspace_bytes < lay.total) return ELASTIC_EWORKSPACE;
-  if (total_tokens == 0) return ELASTIC_OK;
+  if (total_q == 0) return ELASTIC_OK;
 
   const int G = n_q_heads / n_kv_heads;
   const int BT = tokens_per_item(attn_rows_per_item(dtype), G);
   const int BK = attn_key_tile(dtype);
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
   const Pattern pat = to_pattern(sparse);
+  const SeqGeom geo{cu_q, cu_k, total_q, total_k, q_pos, k_pos};
   char* ws = static_cast<char*>(workspace);
   int32_t* n_items = reinterpret_cast<int32_t*>(ws + lay.n_items);
   WorkItem* items = reinterpret_cast<WorkItem*>(ws + lay.items);
   int32_t* tile_prefix = reinterpret_cast<int32_t*>(ws + lay.tile_prefix);
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  char where[96];
 
-  hipError_t e = launch_plan(cu_seqlens, batch, total_tokens, n_kv_heads, head_mask, pat, BT, BK,
-                             max_items, tile_prefix, items, n_items, st);
-  if (e != hipSuccess) return hip_fail(e, "elastic_attn_prefill: plan");
+  hipError_t e = launch_plan(geo, batch, n_kv_heads, head_mask, pat, BT, BK, max_items,
+                             tile_prefix, items, n_items, st);
+  if (e != hipSuccess) {
+    snprintf(where, sizeof(where), "%s: plan", who);
+    return hip_fail(e, where);
+  }
   if (dtype == ELASTIC_BF16)
-    e = launch_attn_bf16(head_dim, q, k, v, o, lse_out, cu_seqlens, total_tokens, n_q_heads,
-                         n_kv_heads, BT, scale, head_mask, pat, items, n_items, max_items, st);
+    e = launch_attn_bf16(head_dim, q, k, v, o, lse_out, geo, n_q_heads, n_kv_heads, BT, scale,
+                         head_mask, pat, items, n_items, max_items, st);
   else
-    e = launch_attn_f32(head_dim, q, k, v, o, lse_out, cu_seqlens, total_tokens, n_q_heads,
-                        n_kv_heads, BT, scale, head_mask, pat, items, n_items, max_items, st);
-  if (e != hipSuccess) return hip_fail(e, "elastic_attn_prefill: attention");
+    e = launch_attn_f32(head_dim, q, k, v, o, lse_out, geo, n_q_heads, n_kv_heads, BT, scale,
+                        head_mask, pat, items, n_items, max_items, st);
+  if (e != hipSuccess) {
+    snprintf(where, sizeof(where), "%s: attention", who);
+    return hip_fail(e, where);
+  }
+  return ELASTIC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int elastic_attn_prefill(const void* q, const void* k, const void* v, void* o, int32_t dtype,
+                         const int32_t* cu_seqlens, int32_t batch, int64_t total_tokens,
+                         int32_t max_seqlen, int32_t n_q_heads, int32_t n_kv_heads,
+                         int32_t head_dim, float softmax_scale, const int32_t* head_mask,
+                         const elastic_sparse_cfg* sparse, float* lse_out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return attn_call("elastic_attn_prefill", q, k, v, o, dtype, cu_seqlens, cu_seqlens, batch,
+                   total_tokens, total_tokens, max_seqlen, max_seqlen, 0, 0, n_q_heads, n_kv_heads,
+                   head_dim, softmax_scale, head_mask, sparse, lse_out, workspace, workspace_bytes,
+                   stream);
+}
+
+int elastic_attn_prefill_kv(const void* q, const void* k, const void* v, void* o, int32_t dtype,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                            int32_t batch, int64_t total_q, int64_t total_k,
+                            int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t q_pos,
+                            int32_t k_pos, int32_t n_q_heads, int32_t n_kv_heads,
+                            int32_t head_dim, float softmax_scale, const int32_t* head_mask,
+                            const elastic_sparse_cfg* sparse, float* lse_out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return attn_call("elastic_attn_prefill_kv", q, k, v, o, dtype, cu_seqlens_q, cu_seqlens_k,
+                   batch, total_q, total_k, max_seqlen_q, max_seqlen_k, q_pos, k_pos, n_q_heads,
+                   n_kv_heads, head_dim, softmax_scale, head_mask, sparse, lse_out, workspace,
+                   workspace_bytes, stream);
+}
+
+int elastic_lse_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                      void* o_out, float* lse_out, int32_t dtype, int64_t rows, int32_t n_heads,
+                      int32_t head_dim, void* stream) {
+  if (rows < 0 || n_heads < 1) return ELASTIC_EINVAL;
+  if (dtype != ELASTIC_BF16 && dtype != ELASTIC_FP32) return ELASTIC_EUNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return ELASTIC_EUNSUPPORTED;
+  if (rows == 0) return ELASTIC_OK;
+  if (!o_a || !lse_a || !o_b || !lse_b || !o_out || !lse_out) return ELASTIC_EINVAL;
+  const hipError_t e = launch_lse_merge(dtype, o_a, lse_a, o_b, lse_b, o_out, lse_out, rows,
+                                        n_heads, head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "elastic_lse_merge");
   return ELASTIC_OK;
 }
 

@@ -24,6 +24,34 @@ struct Pattern {
   int block, sink_blocks, local_blocks, stride_blocks;
 };
 
+// Query/key geometry of one attention call.  Sequence b has queries at rows
+// [cu_q[b], cu_q[b+1]) of q/o and keys at rows [cu_k[b], cu_k[b+1]) of k/v (a null array
+// means one sequence of total_q / total_k rows).  Positions are absolute: query t of the
+// sequence sits at q_pos + t (q_pos < 0: the queries are the last key positions,
+// k_pos + n_k - n_q) and key j at k_pos + j (k_pos a multiple of 64).
+struct SeqGeom {
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int64_t total_q, total_k;
+  int q_pos, k_pos;
+};
+
+struct SeqSpan {
+  int64_t q0, k0;  // first row of the sequence in q/o and in k/v
+  int nq, nk;      // query and key rows
+  int qp;          // absolute position of query row 0
+};
+
+__host__ __device__ inline SeqSpan seq_span(const SeqGeom& g, int b) {
+  SeqSpan s;
+  s.q0 = g.cu_q ? g.cu_q[b] : 0;
+  s.nq = g.cu_q ? g.cu_q[b + 1] - (int)s.q0 : (int)g.total_q;
+  s.k0 = g.cu_k ? g.cu_k[b] : 0;
+  s.nk = g.cu_k ? g.cu_k[b + 1] - (int)s.k0 : (int)g.total_k;
+  s.qp = g.q_pos >= 0 ? g.q_pos : g.k_pos + s.nk - s.nq;
+  return s;
+}
+
 // One scheduled unit of attention work.
 struct WorkItem {
   int seq;    // sequence index b
@@ -42,19 +70,31 @@ __host__ __device__ inline bool key_allowed(int mode, const Pattern& p, int i, i
          (p.stride_blocks > 0 && kb % p.stride_blocks == 0);
 }
 
-// Key tiles visited by the query tokens [t0, t1] (inclusive) of one work item.  M is the
-// mode when it is known at compile time (MODE_*), or -1 to take it from the constructor.
+// Key tiles visited by the query tokens [t0, t1] (inclusive) of one work item.  Positions
+// are absolute: queries and keys of a sequence share one axis, so a chunk of queries can
+// attend a range of keys [k_begin, k_end) (k_begin a multiple of BK, and of the block size
+// for the block pattern).  Tile index kt holds keys [kt * BK, kt * BK + BK).  M is the mode
+// when it is known at compile time (MODE_*), or -1 to take it from the constructor.
 template <int M = -1>
 struct KeyTilesT {
-  int mode_rt, BK, t0, t1, last;
+  int mode_rt, BK, t0, t1;
+  int diag;                 // tile of the last query: the causal limit
+  int lo, last;             // visited tiles lie in [lo, last]; last < lo when none
+  int k_end;                // one past the last key present
   Pattern p;
-  int sink_end, win_begin;  // streaming: tiles [0, sink_end) and [win_begin, last]
+  int sink_end, win_begin;  // streaming: tiles [0, sink_end) and [win_begin, diag]
   int tpb, qb0, qb1;        // block: tiles per block, query blocks of t0 and t1
 
   __host__ __device__ int mode() const { return M >= 0 ? M : mode_rt; }
 
-  __host__ __device__ KeyTilesT(int mode_, const Pattern& p_, int t0_, int t1_, int BK_)
-      : mode_rt(mode_), BK(BK_), t0(t0_), t1(t1_), last(t1_ / BK_), p(p_) {
+  __host__ __device__ KeyTilesT(int mode_, const Pattern& p_, int t0_, int t1_, int BK_,
+                                int k_begin = 0, int k_end_ = 0x7fffffff)
+      : mode_rt(mode_), BK(BK_), t0(t0_), t1(t1_), diag(t1_ >= 0 ? t1_ / BK_ : -1), k_end(k_end_), p(p_) {
+    // (queries at negative positions -- more query rows than keys under bottom-right
+    // alignment -- see no key: their tiles are skipped or fully masked)
+    lo = k_begin / BK;
+    const int hi = k_end > k_begin ? (k_end - 1) / BK : lo - 1;
+    last = diag < hi ? diag : hi;
     sink_end = 0;
     win_begin = 0;
     tpb = 1;
@@ -84,6 +124,7 @@ struct KeyTilesT {
 
   // Smallest visited tile >= kt, or -1 when there is none.
   __host__ __device__ int next(int kt) const {
+    if (kt < lo) kt = lo;
     if (kt > last) return -1;
     if (mode() == MODE_STREAM) {
       if (kt >= sink_end && kt < win_begin) kt = win_begin;
@@ -98,7 +139,8 @@ struct KeyTilesT {
   // Does tile kt need per-element masking for some (query, key) pair of this item?
   __host__ __device__ bool needs_mask(int kt) const {
     const int k0 = kt * BK, k1 = k0 + BK - 1;
-    if (k1 > t0) return true;  // causal edge (also covers keys past the sequence end)
+    if (k1 > t0) return true;      // causal edge
+    if (k1 >= k_end) return true;  // keys past the end of the range (or of the sequence)
     if (mode() == MODE_FULL) return false;
     if (mode() == MODE_STREAM) return !(k1 < p.sink || k0 > t1 - p.window);
     const int kb = k0 / p.block;
@@ -106,27 +148,37 @@ struct KeyTilesT {
              (p.stride_blocks > 0 && kb % p.stride_blocks == 0));
   }
 
-  __host__ __device__ int count() const {
-    if (mode() == MODE_FULL) return last + 1;
-    if (mode() == MODE_STREAM) {  // [0, sink_end) U [win_begin, last], clipped to [0, last]
-      const int se = sink_end < last + 1 ? sink_end : last + 1;
+  // Visited tiles in [0, x] for x <= diag, ignoring the key range, without enumeration.
+  __host__ __device__ int cnt_upto(int x) const {
+    if (x < 0) return 0;
+    if (mode() == MODE_FULL) return x + 1;
+    if (mode() == MODE_STREAM) {  // [0, sink_end) U [win_begin, diag], clipped to [0, diag]
+      const int se = sink_end < diag + 1 ? sink_end : diag + 1;
       const int wb = win_begin > se ? win_begin : se;
-      return se + (last >= wb ? last - wb + 1 : 0);
+      return (x + 1 < se ? x + 1 : se) + (x >= wb ? x - wb + 1 : 0);
     }
-    // block: every tile of each visible key block below qb1, plus the diagonal block's tiles
-    // up to `last`.  Visible blocks below qb1: [0, sink) U [qb0 - local, qb1) U stride
-    // multiples, counted without enumeration.
+    // block: key blocks below qb1 are visible when in [0, a), [b0, qb1) or a stride multiple;
+    // the diagonal block qb1 is visited up to diag
     const int a = p.sink_blocks < qb1 ? p.sink_blocks : qb1;
     const int b0 = qb0 - p.local_blocks > 0 ? qb0 - p.local_blocks : 0;
+    const int xb = x / tpb;
+    const int m = xb < qb1 ? xb : qb1;  // whole visible blocks in [0, m)
     int nb;
     if (a >= b0) {
-      nb = qb1;
+      nb = m;
     } else {
-      nb = a + (qb1 - b0);
-      if (p.stride_blocks > 0)
-        nb += (b0 + p.stride_blocks - 1) / p.stride_blocks - (a + p.stride_blocks - 1) / p.stride_blocks;
+      nb = (m < a ? m : a) + (m > b0 ? m - b0 : 0);
+      const int top = m < b0 ? m : b0;
+      if (p.stride_blocks > 0 && top > a)
+        nb += (top + p.stride_blocks - 1) / p.stride_blocks - (a + p.stride_blocks - 1) / p.stride_blocks;
     }
-    return nb * tpb + (last - qb1 * tpb + 1);
+    if (xb >= qb1) return nb * tpb + (x - qb1 * tpb + 1);
+    const bool vis = xb < a || xb >= b0 || (p.stride_blocks > 0 && xb % p.stride_blocks == 0);
+    return nb * tpb + (vis ? x - xb * tpb + 1 : 0);
+  }
+
+  __host__ __device__ int count() const {
+    return last < lo ? 0 : cnt_upto(last) - cnt_upto(lo - 1);
   }
 };
 using KeyTiles = KeyTilesT<-1>;
@@ -145,22 +197,25 @@ constexpr int F32_BK = 32;
 inline int tokens_per_item(int rows, int G) { return rows / G; }
 
 // ------------------------------------------------------------------ launchers (device code)
-hipError_t launch_plan(const int32_t* cu_seqlens, int batch, int64_t total_tokens, int n_kv_heads,
-                       const int32_t* head_mask, const Pattern& pat, int BT, int BK,
-                       int64_t max_items, int32_t* tile_prefix, WorkItem* items, int32_t* n_items,
-                       hipStream_t stream);
+hipError_t launch_plan(const SeqGeom& geo, int batch, int n_kv_heads, const int32_t* head_mask,
+                       const Pattern& pat, int BT, int BK, int64_t max_items, int32_t* tile_prefix,
+                       WorkItem* items, int32_t* n_items, hipStream_t stream);
 
 hipError_t launch_attn_bf16(int head_dim, const void* q, const void* k, const void* v, void* o,
-                            float* lse, const int32_t* cu_seqlens, int64_t total_tokens,
-                            int n_q_heads, int n_kv_heads, int BT, float scale,
-                            const int32_t* head_mask, const Pattern& pat, const WorkItem* items,
-                            const int32_t* n_items, int64_t grid, hipStream_t stream);
+                            float* lse, const SeqGeom& geo, int n_q_heads, int n_kv_heads, int BT,
+                            float scale, const int32_t* head_mask, const Pattern& pat,
+                            const WorkItem* items, const int32_t* n_items, int64_t grid,
+                            hipStream_t stream);
 
 hipError_t launch_attn_f32(int head_dim, const void* q, const void* k, const void* v, void* o,
-                           float* lse, const int32_t* cu_seqlens, int64_t total_tokens,
-                           int n_q_heads, int n_kv_heads, int BT, float scale,
-                           const int32_t* head_mask, const Pattern& pat, const WorkItem* items,
-                           const int32_t* n_items, int64_t grid, hipStream_t stream);
+                           float* lse, const SeqGeom& geo, int n_q_heads, int n_kv_heads, int BT,
+                           float scale, const int32_t* head_mask, const Pattern& pat,
+                           const WorkItem* items, const int32_t* n_items, int64_t grid,
+                           hipStream_t stream);
+
+hipError_t launch_lse_merge(int dtype, const void* o_a, const float* lse_a, const void* o_b,
+                            const float* lse_b, void* o_out, float* lse_out, int64_t rows,
+                            int heads, int head_dim, hipStream_t stream);
 
 // Router: rows of sequence b are pooled in slabs of ROUTE_SLAB rows.
 constexpr int ROUTE_SLAB = 128;

@@ -1,5 +1,8 @@
 // Scheduler: turns (sequence, KV head, query tile) units and the device-resident head mask
-// into one work list, heaviest first, for the single hybrid attention launch.
+// into one work list, heaviest first, for the single hybrid attention launch.  Query tiles
+// cover each sequence's query rows; costs count the key tiles of the sequence's key range
+// that the tile's queries may see (absolute positions, so query chunks and key ranges cost
+// what they visit).
 //
 // The pages describe the deployment problem this solves: mixed full and sparse heads are
 // slow when run as separate passes on one GPU, so routing metadata goes straight into one
@@ -21,14 +24,15 @@ constexpr int PLAN_LDS_SEQ = 2048;   // sequences whose lengths / tile offsets a
 constexpr int PLAN_LDS_MASK = 16384; // head-mask entries cached in LDS
 
 __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
-    const int32_t* __restrict__ cu_seqlens, int batch, int64_t total_tokens, int n_kv_heads,
-    const int32_t* __restrict__ head_mask, Pattern pat, int BT, int BK, int64_t max_items,
-    int32_t* __restrict__ tile_prefix, WorkItem* __restrict__ items, int32_t* __restrict__ n_items) {
+    SeqGeom geo, int batch, int n_kv_heads, const int32_t* __restrict__ head_mask, Pattern pat,
+    int BT, int BK, int64_t max_items, int32_t* __restrict__ tile_prefix,
+    WorkItem* __restrict__ items, int32_t* __restrict__ n_items) {
   __shared__ int hist[PLAN_BUCKETS];
   __shared__ int cursor[PLAN_BUCKETS];
   __shared__ int scan_tmp[PLAN_THREADS];
   __shared__ int s_prefix[PLAN_LDS_SEQ + 1];
-  __shared__ int s_len[PLAN_LDS_SEQ];
+  __shared__ int s_len[PLAN_LDS_SEQ];   // query rows
+  __shared__ int s_klen[PLAN_LDS_SEQ];  // key rows
   __shared__ unsigned char s_full[PLAN_LDS_MASK];
   __shared__ int carry;
   const int tid = threadIdx.x;
@@ -36,7 +40,10 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
   const bool mask_cached = (int64_t)batch * n_kv_heads <= PLAN_LDS_MASK;
 
   auto seq_len = [&](int b) -> int {
-    return cu_seqlens ? cu_seqlens[b + 1] - cu_seqlens[b] : (int)total_tokens;
+    return geo.cu_q ? geo.cu_q[b + 1] - geo.cu_q[b] : (int)geo.total_q;
+  };
+  auto key_len = [&](int b) -> int {
+    return geo.cu_k ? geo.cu_k[b + 1] - geo.cu_k[b] : (int)geo.total_k;
   };
 
   // 1. tile_prefix[b] = query tiles of the sequences before b (block-wide scan in chunks).
@@ -68,6 +75,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
       if (seq_cached) {
         s_prefix[b] = pre;
         s_len[b] = len;
+        s_klen[b] = key_len(b);
       }
     }
     __syncthreads();
@@ -97,11 +105,13 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     const int b = lo;
     const int qt = tile - (seq_cached ? s_prefix[b] : tile_prefix[b]);
     const int n = seq_cached ? s_len[b] : seq_len(b);
+    const int nk = seq_cached ? s_klen[b] : key_len(b);
+    const int qp = geo.q_pos >= 0 ? geo.q_pos : geo.k_pos + nk - n;  // absolute position of row 0
     const int t0 = qt * BT;
     const int t1 = min(t0 + BT, n) - 1;
     const int mi = b * n_kv_heads + g;
     const bool full = mask_cached ? s_full[mi] != 0 : (head_mask == nullptr || head_mask[mi] != 0);
-    const KeyTiles kt(full ? MODE_FULL : pat.kind, pat, t0, t1, BK);
+    const KeyTiles kt(full ? MODE_FULL : pat.kind, pat, qp + t0, qp + t1, BK, geo.k_pos, geo.k_pos + nk);
     it.seq = b;
     it.group = g;
     it.qtile = qt;
@@ -154,13 +164,11 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
 
 }  // namespace
 
-hipError_t launch_plan(const int32_t* cu_seqlens, int batch, int64_t total_tokens, int n_kv_heads,
-                       const int32_t* head_mask, const Pattern& pat, int BT, int BK,
-                       int64_t max_items, int32_t* tile_prefix, WorkItem* items, int32_t* n_items,
-                       hipStream_t stream) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, cu_seqlens, batch,
-                     total_tokens, n_kv_heads, head_mask, pat, BT, BK, max_items, tile_prefix,
-                     items, n_items);
+hipError_t launch_plan(const SeqGeom& geo, int batch, int n_kv_heads, const int32_t* head_mask,
+                       const Pattern& pat, int BT, int BK, int64_t max_items, int32_t* tile_prefix,
+                       WorkItem* items, int32_t* n_items, hipStream_t stream) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, geo, batch, n_kv_heads,
+                     head_mask, pat, BT, BK, max_items, tile_prefix, items, n_items);
   return hipGetLastError();
 }
 

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define ELASTIC_ABI_VERSION 1
+#define ELASTIC_ABI_VERSION 2
 
 enum elastic_status {
   ELASTIC_OK = 0,
@@ -144,6 +144,55 @@ int elastic_attn_prefill(const void* q, const void* k, const void* v, void* o, i
                          int32_t head_dim, float softmax_scale, const int32_t* head_mask,
                          const elastic_sparse_cfg* sparse, float* lse_out, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/*
+ * Prefill of query rows against a separate range of key rows: chunked prefill and key-range
+ * splits (summary appendix D.1 "Sparse Inference": prefill runs in chunks of 16,384 queries;
+ * the partial results of split key ranges combine with elastic_lse_merge).
+ *
+ * Sequence b owns query rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) of q/o/lse and key rows
+ * [cu_seqlens_k[b], cu_seqlens_k[b+1]) of k/v.  Positions are absolute within the sequence:
+ * query row t sits at q_pos + t and key row j at k_pos + j; every pattern (causal, sink,
+ * window, blocks) is evaluated on these positions and restricted to the keys present.
+ *   q_pos   >= 0: position of every sequence's first query row;
+ *           -1: bottom-right alignment, the queries are the sequence's last key positions
+ *           (q_pos = k_pos + n_k - n_q per sequence): one prefill chunk over its whole prefix.
+ *   k_pos   >= 0, a multiple of 64 (and of block_size for the block pattern).
+ * A query row that sees no key gets o = 0 and lse = -inf.
+ *
+ *  q, o        [total_q, n_q_heads, head_dim];  k, v [total_k, n_kv_heads, head_dim]
+ *  lse_out     [n_q_heads, total_q] fp32, may be NULL
+ *  cu_seqlens_q / cu_seqlens_k  int32 [batch + 1] device arrays; both NULL only when batch == 1
+ *  max_seqlen_q, max_seqlen_k   >= every sequence's query / key rows (sizing and checks)
+ *  workspace   elastic_attn_workspace_size(dtype, batch, total_q, n_q_heads, n_kv_heads,
+ *              head_dim) bytes.
+ * Other arguments, supported shapes and errors as for elastic_attn_prefill;
+ * ELASTIC_EINVAL also for a misaligned k_pos, q_pos < -1, or positions past 2^31 - 1.
+ * elastic_attn_prefill is this call with q = k rows, q_pos = k_pos = 0.
+ */
+int elastic_attn_prefill_kv(const void* q, const void* k, const void* v, void* o, int32_t dtype,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                            int32_t batch, int64_t total_q, int64_t total_k,
+                            int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t q_pos,
+                            int32_t k_pos, int32_t n_q_heads, int32_t n_kv_heads,
+                            int32_t head_dim, float softmax_scale, const int32_t* head_mask,
+                            const elastic_sparse_cfg* sparse, float* lse_out, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
+ * Combines two attention results of the same query rows over disjoint key sets (for example
+ * the two halves of a split key range, or a sequence shard's partial and its halo part):
+ *   lse = log(exp(lse_a) + exp(lse_b)),  o = exp(lse_a - lse) o_a + exp(lse_b - lse) o_b,
+ * per (row, head); a row with lse_a = lse_b = -inf stays o = 0, lse = -inf.
+ *
+ *  o_a, o_b, o_out        [rows, n_heads, head_dim], dtype (bf16 or fp32)
+ *  lse_a, lse_b, lse_out  [n_heads, rows] fp32 natural log (the layout elastic_attn_* write)
+ * o_out / lse_out may alias o_a or o_b / lse_a or lse_b (in-place merge).  All pointers are
+ * device pointers and required; head_dim 64 or 128.  Enqueues one elementwise kernel.
+ */
+int elastic_lse_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                      void* o_out, float* lse_out, int32_t dtype, int64_t rows, int32_t n_heads,
+                      int32_t head_dim, void* stream);
 
 /*
  * Host-only work counter (no HIP call): the number of allowed (query, key) score entries

@@ -1,5 +1,6 @@
 """fp64 CPU oracle (test infrastructure only; never on the product path)."""
 from .elastic_oracle import (  # noqa: F401
-    allowed, as_f64, attention, decode_bf16, effective_flops, effective_sparsity, entries,
-    head_modes, mean_exact, model_sparsity_ratio, pooled_rows, route, row_key_counts,
+    allowed, as_f64, attention, attention_kv, block_streaming, chunked_prefill, decode_bf16,
+    effective_flops, effective_sparsity, entries, head_modes, lse_merge, mean_exact,
+    model_sparsity_ratio, pooled_rows, route, row_key_counts,
 )

@@ -74,6 +74,48 @@ def test_attention_validation_without_gpu():
     assert _attn(T=0, q=None, k=None, v=None, o=None, wsb=need) == 0  # empty input: no-op
 
 
+def _attn_kv(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dtype=0, cuq=None, cuk=None, batch=1, Tq=256, Tk=512,
+             mq=256, mk=512, qpos=-1, kpos=0, hq=8, hkv=2, D=128, scale=0.0, mask=None,
+             sparse=ext.sparse_cfg({"kind": "streaming", "sink": 4, "window": 64}), lse=None,
+             ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    sp = C.byref(a["sparse"]) if a["sparse"] is not None else None
+    return L.elastic_attn_prefill_kv(a["q"], a["k"], a["v"], a["o"], a["dtype"], a["cuq"], a["cuk"],
+                                     a["batch"], a["Tq"], a["Tk"], a["mq"], a["mk"], a["qpos"],
+                                     a["kpos"], a["hq"], a["hkv"], a["D"], a["scale"], a["mask"], sp,
+                                     a["lse"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_attention_kv_validation_without_gpu():
+    EINVAL, EUNS, EWS = 1, 2, 3
+    assert _attn_kv(kpos=32) == EINVAL            # key range must start on a 64-key tile
+    assert _attn_kv(kpos=-64) == EINVAL
+    assert _attn_kv(qpos=-2) == EINVAL
+    assert _attn_kv(k=None) == EINVAL
+    assert _attn_kv(batch=2, cuq=FAKE, cuk=None) == EINVAL
+    assert _attn_kv(qpos=2 ** 31 - 100) == EINVAL  # positions past int32
+    blk = {"kind": "block", "block": 128, "sink_blocks": 1, "local_blocks": 8, "stride_blocks": 16}
+    assert _attn_kv(sparse=ext.sparse_cfg(blk), kpos=64) == EINVAL  # not block aligned
+    assert _attn_kv(D=80) == EUNS
+    assert _attn_kv(ws=None) == EWS
+    need = ext.attn_workspace_size(0, 1, 256, 8, 2, 128)
+    assert _attn_kv(wsb=need - 1) == EWS
+    assert _attn_kv(Tq=0, q=None, o=None, wsb=need) == 0   # no query rows: no-op
+    assert _attn_kv(Tk=0, k=None, v=None, Tq=0, q=None, o=None, wsb=need) == 0
+
+
+def test_lse_merge_validation_without_gpu():
+    EINVAL, EUNS = 1, 2
+    m = L.elastic_lse_merge
+    assert m(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 10, 0, 128, None) == EINVAL
+    assert m(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, -1, 8, 128, None) == EINVAL
+    assert m(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 10, 8, 96, None) == EUNS
+    assert m(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 5, 10, 8, 128, None) == EUNS
+    assert m(None, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 10, 8, 128, None) == EINVAL
+    assert m(None, None, None, None, None, None, 0, 0, 8, 128, None) == 0  # no rows: no-op
+
+
 def _route(**kw):
     a = dict(hidden=FAKE, dtype=0, cu=None, batch=1, T=1024, d=4096, ph=0, pt=0, w1=FAKE, dr=64,
              w2=FAKE, hkv=8, thr=0.0, logits=None, mask=FAKE, ws=FAKE, wsb=1 << 30, stream=None)

@@ -1,7 +1,7 @@
 // Host-side exhaustive check of the key-tile schedule used by the scheduler and the attention
-// kernels: every (query, key) pair a work item may attend lies in a visited tile, tiles are
-// visited in increasing order, the visit count matches count(), and a tile reported as
-// mask-free holds only visible pairs.
+// kernels: every (query, key) pair a work item may attend within its key range lies in a
+// visited tile, tiles are visited in increasing order and inside the range, the visit count
+// matches the closed-form count(), and a tile reported as mask-free holds only visible pairs.
 #include <cstdio>
 #include <vector>
 
@@ -28,36 +28,45 @@ int main() {
           const bool full = pi == pats.size();
           const Pattern p = full ? pats[0] : pats[pi];
           const int mode = full ? MODE_FULL : p.kind;
-          for (int t0 = 0; t0 < n; t0 += BT) {
-            const int t1 = (t0 + BT < n ? t0 + BT : n) - 1;
-            KeyTiles kt(mode, p, t0, t1, BK);
-            std::vector<char> vis((n + BK - 1) / BK + 2, 0);
-            int prev = -1, cnt = 0;
-            for (int t = kt.next(0); t >= 0; t = kt.next(t + 1)) {
-              if (t <= prev) fail("order", mode, t0, t1, BK, t);
-              if (t >= (int)vis.size()) { fail("range", mode, t0, t1, BK, t); break; }
-              vis[t] = 1; prev = t; ++cnt;
-              if (!kt.needs_mask(t)) {
-                for (int i = t0; i <= t1; ++i)
-                  for (int j = t * BK; j < t * BK + BK; ++j)
-                    if (j >= n || !key_allowed(mode, p, i, j)) { fail("maskfree", mode, t0, t1, BK, t); i = t1 + 1; break; }
+          // key ranges [kb, ke) on the same axis as the queries: the whole sequence, a prefix,
+          // an aligned suffix and an aligned middle piece (kb aligned to the tile and block)
+          const int align = (mode == MODE_BLOCK && p.block > BK) ? p.block : BK;
+          const int mid = (n / 2 / align) * align;
+          const int ranges[][2] = {{0, n}, {0, n / 2 + 1}, {mid, n}, {mid, mid + n / 3 + 1}};
+          for (auto& rg : ranges) {
+            const int kb = rg[0], ke = rg[1] < n ? rg[1] : n;
+            if (kb != 0 && kb == mid && mid == 0 && rg[1] == n) continue;  // duplicate of the first
+            for (int t0 = 0; t0 < n; t0 += BT) {
+              const int t1 = (t0 + BT < n ? t0 + BT : n) - 1;
+              KeyTiles kt(mode, p, t0, t1, BK, kb, ke);
+              std::vector<char> vis((n + BK - 1) / BK + 2, 0);
+              int prev = -1, cnt = 0;
+              for (int t = kt.next(0); t >= 0; t = kt.next(t + 1)) {
+                if (t <= prev) fail("order", mode, t0, t1, BK, t);
+                if (t >= (int)vis.size() || t * BK < kb || t * BK >= ke) { fail("range", mode, t0, t1, BK, t); break; }
+                vis[t] = 1; prev = t; ++cnt;
+                if (!kt.needs_mask(t)) {
+                  for (int i = t0; i <= t1; ++i)
+                    for (int j = t * BK; j < t * BK + BK; ++j)
+                      if (j >= ke || !key_allowed(mode, p, i, j)) { fail("maskfree", mode, t0, t1, BK, t); i = t1 + 1; break; }
+                }
               }
+              if (cnt != kt.count()) fail("count", mode, t0, t1, BK, cnt);
+              // the compile-time-mode instances walk the same tiles
+              for (int t = 0; t <= kt.diag + 1; ++t) {
+                int a = -2, b = -2; bool ma = false, mb = false;
+                if (mode == MODE_FULL) { KeyTilesT<MODE_FULL> s(mode, p, t0, t1, BK, kb, ke); a = s.next(t); if (a >= 0) ma = s.needs_mask(a); }
+                else if (mode == MODE_STREAM) { KeyTilesT<MODE_STREAM> s(mode, p, t0, t1, BK, kb, ke); a = s.next(t); if (a >= 0) ma = s.needs_mask(a); }
+                else { KeyTilesT<MODE_BLOCK> s(mode, p, t0, t1, BK, kb, ke); a = s.next(t); if (a >= 0) ma = s.needs_mask(a); }
+                b = kt.next(t); if (b >= 0) mb = kt.needs_mask(b);
+                if (a != b || ma != mb) { fail("static-mode", mode, t0, t1, BK, t); break; }
+              }
+              for (int i = t0; i <= t1; ++i)
+                for (int j = kb; j <= i && j < ke; ++j)
+                  if (key_allowed(mode, p, i, j) && !vis[j / BK]) { fail("missed", mode, t0, t1, BK, j / BK); i = t1 + 1; break; }
+              if (kb == 0 && ke == n && !vis[t0 / BK]) fail("diag", mode, t0, t1, BK, t0 / BK);
+              ++checked;
             }
-            if (cnt != kt.count()) fail("count", mode, t0, t1, BK, cnt);
-            // the compile-time-mode instances walk the same tiles
-            for (int t = 0; t <= kt.last + 1; ++t) {
-              int a = -2, b = -2; bool ma = false, mb = false;
-              if (mode == MODE_FULL) { KeyTilesT<MODE_FULL> s(mode, p, t0, t1, BK); a = s.next(t); if (a >= 0) ma = s.needs_mask(a); }
-              else if (mode == MODE_STREAM) { KeyTilesT<MODE_STREAM> s(mode, p, t0, t1, BK); a = s.next(t); if (a >= 0) ma = s.needs_mask(a); }
-              else { KeyTilesT<MODE_BLOCK> s(mode, p, t0, t1, BK); a = s.next(t); if (a >= 0) ma = s.needs_mask(a); }
-              b = kt.next(t); if (b >= 0) mb = kt.needs_mask(b);
-              if (a != b || ma != mb) { fail("static-mode", mode, t0, t1, BK, t); break; }
-            }
-            for (int i = t0; i <= t1; ++i)
-              for (int j = 0; j <= i; ++j)
-                if (key_allowed(mode, p, i, j) && !vis[j / BK]) { fail("missed", mode, t0, t1, BK, j / BK); i = t1 + 1; break; }
-            if (!vis[t0 / BK]) fail("diag", mode, t0, t1, BK, t0 / BK);
-            ++checked;
           }
         }
       }
