@@ -168,6 +168,8 @@ def main():
 
     if not args.no_supplements:
         rec["supplements"] = supplements(ext, torch, w, q, k, v, o, cu, ws_attn, stream, args)
+        if w.batch == 1:
+            rec["supplements"]["deployment"] = deployment(ext, torch, w, q, k, v, o, mask, ws_attn, stream)
         del q, k, v, o
         if has_router:
             del hidden
@@ -208,6 +210,55 @@ def _time_attn(ext, torch, stream, fn, reps=10, warm=3):
     b.record(stream)
     torch.cuda.synchronize()
     return a.elapsed_time(b) / reps
+
+
+def deployment(ext, torch, w, q, k, v, o, mask, ws, stream):
+    """The pages' inference settings on the same 32K layer and router mask: prefill in chunks
+    of 16,384 queries (each chunk over its whole prefix) against one launch, a key range
+    split in two and merged by LSE, the merge kernel's bandwidth, and block-granular
+    streaming (block 64, 128 sink tokens, window 1024) on every head."""
+    T, hq, D = q.shape
+    hkv = k.shape[1]
+    mask_h = mask.cpu().numpy()
+    ent = ext.attn_entries([T], mask_h, hq, hkv, w.sparse)
+    lse = torch.empty((hq, T), dtype=torch.float32, device=q.device)
+    one = _time_attn(ext, torch, stream, lambda: ext.attn_prefill(
+        q, k, v, max_seqlen=T, head_mask=mask, sparse=w.sparse, out=o, lse=lse, workspace=ws))
+    C = 16384
+
+    lse_c = torch.empty((hq, C), dtype=torch.float32, device=q.device)  # [heads, chunk rows]
+
+    def chunked():
+        for c0 in range(0, T, C):
+            c1 = min(T, c0 + C)
+            ext.attn_prefill_kv(q[c0:c1], k[:c1], v[:c1], head_mask=mask, sparse=w.sparse,
+                                out=o[c0:c1], lse=lse_c[:, :c1 - c0], workspace=ws)
+    ms_chunk = _time_attn(ext, torch, stream, chunked)
+    oa, ob = torch.empty_like(o), torch.empty_like(o)
+    la, lb = torch.empty_like(lse), torch.empty_like(lse)
+
+    def split():
+        ext.attn_prefill_kv(q, k[:C], v[:C], q_pos=0, k_pos=0, head_mask=mask, sparse=w.sparse,
+                            out=oa, lse=la, workspace=ws)
+        ext.attn_prefill_kv(q, k[C:], v[C:], q_pos=0, k_pos=C, head_mask=mask, sparse=w.sparse,
+                            out=ob, lse=lb, workspace=ws)
+        ext.lse_merge(oa, la, ob, lb, out=o, lse_out=lse)
+    ms_split = _time_attn(ext, torch, stream, split)
+    ms_merge = _time_attn(ext, torch, stream, lambda: ext.lse_merge(oa, la, ob, lb, out=o, lse_out=lse))
+    merge_bytes = 3 * o.numel() * o.element_size() + 3 * lse.numel() * 4
+    bstream = {"kind": "block", "block": 64, "sink_blocks": 2, "local_blocks": 15, "stride_blocks": 0}
+    zeros = torch.zeros((1, hkv), dtype=torch.int32, device=q.device)
+    ms_bs = _time_attn(ext, torch, stream, lambda: ext.attn_prefill(
+        q, k, v, max_seqlen=T, head_mask=zeros, sparse=bstream, out=o, workspace=ws))
+    ent_bs = ext.attn_entries([T], [[0] * hkv], hq, hkv, bstream)
+    return {"one_launch_ms": round(one, 4),
+            "chunked_16384_ms": round(ms_chunk, 4),
+            "chunked_tflops": round(4 * D * ent / ms_chunk / 1e9, 2),
+            "key_split_merge_ms": round(ms_split, 4),
+            "lse_merge_us": round(ms_merge * 1e3, 2),
+            "lse_merge_gbs": round(merge_bytes / (ms_merge * 1e-3) / 1e9, 1),
+            "block_streaming_b64_s128_w1024_ms": round(ms_bs, 4),
+            "block_streaming_tflops": round(4 * D * ent_bs / ms_bs / 1e9, 2)}
 
 
 def supplements(ext, torch, w, q, k, v, o, cu, ws, stream, args):
