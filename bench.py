@@ -170,6 +170,9 @@ def main():
         rec["supplements"] = supplements(ext, torch, w, q, k, v, o, cu, ws_attn, stream, args)
         if w.batch == 1:
             rec["supplements"]["deployment"] = deployment(ext, torch, w, q, k, v, o, mask, ws_attn, stream)
+        if has_router:
+            rec["supplements"]["router"] = router_detail(ext, torch, hidden, w1, w2, cu, threshold,
+                                                         logits, mask.clone(), ws_route, stream)
         del q, k, v, o
         if has_router:
             del hidden
@@ -259,6 +262,32 @@ def deployment(ext, torch, w, q, k, v, o, mask, ws, stream):
             "lse_merge_gbs": round(merge_bytes / (ms_merge * 1e-3) / 1e9, 1),
             "block_streaming_b64_s128_w1024_ms": round(ms_bs, 4),
             "block_streaming_tflops": round(4 * D * ent_bs / ms_bs / 1e9, 2)}
+
+
+def router_detail(ext, torch, hidden, w1, w2, cu, threshold, logits, mask, ws, stream, reps=10):
+    """Router alone with the 256 MB MALL flushed before every call (a 1 GiB read in between,
+    outside the timed events, so the cache holds clean unrelated lines): mean pooling over all
+    rows, and boundary pooling of the first and last 100 rows (appendix H.4 of the summary)."""
+    scratch = torch.zeros(1 << 28, dtype=torch.float32, device=hidden.device)
+    out = {}
+    T, d = hidden.shape
+    for name, ph, pt in (("mean_pool", 0, 0), ("boundary_pool_100_100", 100, 100)):
+        times = []
+        for r in range(reps + 2):
+            scratch.sum()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            ext.route(hidden, w1, w2, cu_seqlens=cu, threshold=threshold, pool_head=ph, pool_tail=pt,
+                      logits=logits, mask=mask, workspace=ws)
+            b.record(stream)
+            torch.cuda.synchronize()
+            if r >= 2:
+                times.append(a.elapsed_time(b) * 1e3)
+        us = float(np.median(times))
+        rows = T if ph == 0 else min(T, (ph + pt) * (cu.numel() - 1))
+        out[name] = {"us_median": round(us, 2), "hbm_gbs": round(rows * d * 2 / (us * 1e-6) / 1e9, 1)}
+    del scratch
+    return out
 
 
 def supplements(ext, torch, w, q, k, v, o, cu, ws, stream, args):

@@ -69,7 +69,7 @@ __device__ inline void load8(const void* hidden, int dtype, int64_t off, float* 
 // Partial column sums of one slab: partials[slab, col].
 __global__ __launch_bounds__(RT) void route_pool_partial(
     const void* __restrict__ hidden, int dtype, const int32_t* __restrict__ cu, int batch,
-    int64_t total, int d, int pool_head, int pool_tail, float* __restrict__ partials,
+    int64_t total, int d, int pool_head, int pool_tail, int slab_rows, float* __restrict__ partials,
     int32_t* __restrict__ counters) {
   __shared__ float red[3][64][8 + 1];
   const int slab = blockIdx.x;
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(RT) void route_pool_partial(
   SeqPool s{};
   for (int bb = 0; bb < batch; ++bb) {
     s = seq_pool(cu, bb, total, pool_head, pool_tail);
-    const int ns = (s.m + ROUTE_SLAB - 1) / ROUTE_SLAB;
+    const int ns = (s.m + slab_rows - 1) / slab_rows;
     if (slab < acc + ns) {
       b = bb;
       slab_in = slab - acc;
@@ -90,8 +90,8 @@ __global__ __launch_bounds__(RT) void route_pool_partial(
   if (b < 0) return;  // past the last slab of the batch
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = blockIdx.y * RCOLS + lane * 8;
-  const int p0 = slab_in * ROUTE_SLAB;
-  const int p1 = min(s.m, p0 + ROUTE_SLAB);
+  const int p0 = slab_in * slab_rows;
+  const int p1 = min(s.m, p0 + slab_rows);
   float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (col < d) {
     int p = p0 + wave;
@@ -138,7 +138,7 @@ constexpr int HW = HT / 64;
 
 __global__ __launch_bounds__(HT) void route_head(
     const float* __restrict__ partials, const int32_t* __restrict__ cu, int batch, int64_t total,
-    int d, int pool_head, int pool_tail, const float* __restrict__ w1, int d_router,
+    int d, int pool_head, int pool_tail, int slab_rows, const float* __restrict__ w1, int d_router,
     const float* __restrict__ w2, int n_kv_heads, float threshold, float* __restrict__ zpart,
     int32_t* __restrict__ counters, float* __restrict__ logits, int32_t* __restrict__ mask) {
   __shared__ float red[HW][HCOLS];
@@ -150,10 +150,10 @@ __global__ __launch_bounds__(HT) void route_head(
   int first = 0;
   for (int bb = 0; bb < b; ++bb) {
     const SeqPool s = seq_pool(cu, bb, total, pool_head, pool_tail);
-    first += (s.m + ROUTE_SLAB - 1) / ROUTE_SLAB;
+    first += (s.m + slab_rows - 1) / slab_rows;
   }
   const SeqPool sp = seq_pool(cu, b, total, pool_head, pool_tail);
-  const int ns = (sp.m + ROUTE_SLAB - 1) / ROUTE_SLAB;
+  const int ns = (sp.m + slab_rows - 1) / slab_rows;
   const int c0 = ch * HCOLS;
 
   // W1 strip of this workgroup, fetched first so its latency overlaps the partial sums:
@@ -253,15 +253,32 @@ hipError_t launch_route(const void* hidden, int hidden_dtype, const int32_t* cu_
                         float threshold, float* logits_out, int32_t* mask_out, float* partials,
                         int64_t max_slabs, float* zpart, int32_t* counters, hipStream_t stream) {
   const int chunks = (d_model + RCOLS - 1) / RCOLS;
+  // Boundary pooling reads at most pool_head + pool_tail rows per sequence.  Few rows give
+  // few slabs, and a 128-row slab is eight dependent load rounds for its workgroup, so such
+  // calls use 16-row slabs (one round) whenever the workspace, sized for 128-row slabs of
+  // every token, holds them; the grid covers the pooled slabs only.
+  int slab_rows = ROUTE_SLAB;
+  if (pool_head > 0 || pool_tail > 0) {
+    const int64_t pooled = (int64_t)pool_head + pool_tail;
+    const int64_t small = (int64_t)batch * ((pooled + 15) / 16);
+    if (small <= max_slabs) {
+      slab_rows = 16;
+      max_slabs = small;
+    } else {
+      const int64_t per = (pooled + ROUTE_SLAB - 1) / ROUTE_SLAB;
+      if ((int64_t)batch * per < max_slabs) max_slabs = (int64_t)batch * per;
+    }
+  }
   // at least one workgroup: block (0, 0) also clears the completion counters
   hipLaunchKernelGGL(route_pool_partial, dim3((unsigned)(max_slabs > 0 ? max_slabs : 1), chunks),
                      dim3(RT), 0, stream, hidden, hidden_dtype, cu_seqlens, batch, total_tokens,
-                     d_model, pool_head, pool_tail, partials, counters);
+                     d_model, pool_head, pool_tail, slab_rows, partials, counters);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(route_head, dim3(batch, (d_model + HCOLS - 1) / HCOLS), dim3(HT), 0, stream,
-                     partials, cu_seqlens, batch, total_tokens, d_model, pool_head, pool_tail, w1,
-                     d_router, w2, n_kv_heads, threshold, zpart, counters, logits_out, mask_out);
+                     partials, cu_seqlens, batch, total_tokens, d_model, pool_head, pool_tail,
+                     slab_rows, w1, d_router, w2, n_kv_heads, threshold, zpart, counters, logits_out,
+                     mask_out);
   return hipGetLastError();
 }
 
