@@ -39,6 +39,8 @@
 //  * Epilogue: each wave stages its 32 normalised rows in the idle tile slots (same swizzle)
 //    and writes whole O rows with 16-byte stores, so the G heads of a token leave as one
 //    contiguous run instead of scattered 8-byte pieces.
+#include <type_traits>
+
 #include "elastic_internal.hpp"
 
 namespace elastic {
@@ -163,10 +165,20 @@ __device__ __forceinline__ void attn_item(
   // tile kt (absolute) holds key rows [kt * BK - k_pos, +BK) of the sequence; rows past the
   // key range read as zero through the descriptor's range
   auto tile_rsrc = [&](const uint16_t* base, int kt) {
-    const int rows = min(k_end - kt * BK, BK);
+    const int rows = min(k_end - kt * BK, BK);  // >= 1: the general step loads tiles <= last only
     return __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(base + (int64_t)(kt * BK - geo.k_pos) * kv_row), (short)0,
         rows * (int)kv_row * 2, 0x00020000);
+  };
+  // a tile whole inside the key range: constant descriptor range
+  auto dma_full = [&](const uint16_t* base, int kt, uint16_t* slot, const int (&voff)[CPT]) {
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(base + (int64_t)(kt * BK - geo.k_pos) * kv_row), (short)0,
+        BK * (int)kv_row * 2, 0x00020000);
+#pragma unroll
+    for (int m = 0; m < CPT; ++m)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(slot + (wave * CPT + m) * 512), 16,
+                                               voff[m], 0, 0, 0);
   };
   auto dma = [&](const uint16_t* base, int kt, uint16_t* slot, const int (&voff)[CPT]) {
     const auto rs = tile_rsrc(base, kt);
@@ -289,12 +301,23 @@ __device__ __forceinline__ void attn_item(
 
     // One step on tile j: DMA K_{j+3} and V_{j+2}; S_{j+1} = K_{j+1} Q^T; p_j = exp2(c s_j - m);
     // O += V_j^T P_j^T; mask and maximum of S_{j+1}; wait for the previous step's DMA; barrier.
-    auto step = [&](f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    // STEADY: a step inside a run of consecutive whole tiles where tile j+1 needs no mask (the
+    // key-tile schedule's steady_pair), so no bound, mask or DMA-count decisions are taken:
+    // the scalar work of a step shrinks to the DMA descriptors and one loop test.  Used for
+    // full items, whose tiles below the diagonal form one such run; for the shorter runs of
+    // sparse items the extra loop copy costs more than it saves.
+    auto step = [&](auto steady_tag, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+      constexpr bool STEADY = decltype(steady_tag)::value;
       const int sj1 = sj == NSLOT - 1 ? 0 : sj + 1;
       const int sj2 = sj1 == NSLOT - 1 ? 0 : sj1 + 1;
-      const int n_dma = (kt_n3 >= 0 ? CPT : 0) + (kt_n2 >= 0 ? CPT : 0);
-      if (kt_n3 >= 0) dma(kbase, kt_n3, kslot + sj * SLOT, k_voff);   // slot of K_j, read last step
-      if (kt_n2 >= 0) dma(vbase, kt_n2, vslot + sj2 * SLOT, v_voff);  // slot of V_{j-1}, read last step
+      const int n_dma = STEADY ? 2 * CPT : (kt_n3 >= 0 ? CPT : 0) + (kt_n2 >= 0 ? CPT : 0);
+      if (STEADY) {
+        dma_full(kbase, kt_n3, kslot + sj * SLOT, k_voff);
+        dma_full(vbase, kt_n2, vslot + sj2 * SLOT, v_voff);
+      } else {
+        if (kt_n3 >= 0) dma(kbase, kt_n3, kslot + sj * SLOT, k_voff);   // slot of K_j, read last step
+        if (kt_n2 >= 0) dma(vbase, kt_n2, vslot + sj2 * SLOT, v_voff);  // slot of V_{j-1}, read last step
+      }
       if (pending) {
         l_run *= alpha;
 #pragma unroll
@@ -303,7 +326,7 @@ __device__ __forceinline__ void attn_item(
           for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
         pending = false;
       }
-      const bool has_next = kt_n1 >= 0;
+      const bool has_next = STEADY || kt_n1 >= 0;
       // Region 1: Q.K^T of tile j+1 (NQK MFMAs; K fragments read three ahead) with the exp2,
       // bf16 packing and row sums of tile j placed between them.
       constexpr int NQK = 2 * DC, NPV = 4 * DB;
@@ -341,7 +364,7 @@ __device__ __forceinline__ void attn_item(
       // keep tile j's weights in this region (no sinking past the mask branch)
       asm volatile("" ::"v"(pop[0][0]), "v"(pop[0][1]), "v"(pop[1][0]), "v"(pop[1][1]), "v"(ls[0]),
                    "v"(ls[1]), "v"(ls[2]), "v"(ls[3]));
-      if (has_next && tiles.needs_mask(kt_n1)) apply_mask(sn, kt_n1);
+      if (!STEADY && has_next && tiles.needs_mask(kt_n1)) apply_mask(sn, kt_n1);
       // Region 2: P.V of tile j (NPV MFMAs; transposing V reads two fragments ahead) with the
       // maximum of tile j+1 placed between them.
       {
@@ -389,7 +412,7 @@ __device__ __forceinline__ void attn_item(
           pending = true;
         }
       }
-      const int kt_n4 = kt_n3 >= 0 ? tiles.next(kt_n3 + 1) : -1;
+      const int kt_n4 = STEADY ? kt_n3 + 1 : (kt_n3 >= 0 ? tiles.next(kt_n3 + 1) : -1);
       // this step's DMA may stay in flight; the previous step's (K_{j+2}, V_{j+1}) must land
       if (n_dma == 2 * CPT) WAIT_VMCNT(2 * CPT);
       else if (n_dma == CPT) WAIT_VMCNT(CPT);
@@ -404,10 +427,21 @@ __device__ __forceinline__ void attn_item(
       sj = sj1;
     };
 
+    using SteadyT = std::integral_constant<bool, true>;
+    using GeneralT = std::integral_constant<bool, false>;
+    if (MODE == MODE_FULL) {
+      // Full items visit consecutive tiles.  A pair of steady steps from tile j loads tiles up
+      // to j+4 (whole inside the key range), advances the schedule to j+5 (a visited tile) and
+      // computes S of tiles j+1, j+2 (below the diagonal and the key range's end: no mask).
+      while (tiles.steady_pair(kt_cur)) {
+        step(SteadyT{}, s0, s1);
+        step(SteadyT{}, s1, s0);
+      }
+    }
     while (true) {
-      step(s0, s1);
+      step(GeneralT{}, s0, s1);
       if (kt_cur < 0) break;
-      step(s1, s0);
+      step(GeneralT{}, s1, s0);
       if (kt_cur < 0) break;
     }
   }

@@ -180,6 +180,23 @@ struct KeyTilesT {
   __host__ __device__ int count() const {
     return last < lo ? 0 : cnt_upto(last) - cnt_upto(lo - 1);
   }
+
+  // May a pair of steady steps start at visited tile j?  Then tiles j..j+5 are visited
+  // consecutively, tiles j..j+4 hold BK keys of the range each, and tiles j+1, j+2 need no
+  // mask: the pair loads, computes and advances without any bound decision.  Such runs are
+  // a full item's tiles below the diagonal, a streaming item's window interior, and the
+  // local blocks every query of a block item sees.
+  __host__ __device__ bool steady_pair(int j) const {
+    const int whole_end = k_end / BK;
+    const int causal = (t0 + 1) / BK;  // tiles below hold only keys <= t0
+    const int mask_from = causal < whole_end ? causal : whole_end;
+    if (!(j + 5 <= last && j + 4 < whole_end && j + 2 < mask_from)) return false;
+    if (mode() == MODE_FULL) return true;
+    if (mode() == MODE_STREAM) return j >= win_begin && (j + 1) * BK > t1 - p.window;
+    const int run = (qb0 - p.local_blocks > 0 ? qb0 - p.local_blocks : 0) * tpb;
+    const int free = (qb1 - p.local_blocks > 0 ? qb1 - p.local_blocks : 0) * tpb;
+    return j >= run && j + 1 >= free;
+  }
 };
 using KeyTiles = KeyTilesT<-1>;
 

@@ -20,7 +20,7 @@ int main() {
   for (auto& s : SW) pats.push_back(Pattern{ELASTIC_SPARSE_STREAMING, s[0], s[1], 64, 0, 0, 0});
   const int BL[][4] = {{64, 1, 2, 3}, {128, 1, 8, 16}, {128, 0, 1, 0}, {64, 0, 0, 0}, {64, 3, 1, 2}, {128, 2, 0, 1}};
   for (auto& b : BL) pats.push_back(Pattern{ELASTIC_SPARSE_BLOCK, 0, 1, b[0], b[1], b[2], b[3]});
-  long checked = 0;
+  long checked = 0, steady = 0;
   for (int BK : {32, 64}) {
     for (int n : {1, 5, 63, 64, 65, 300, 1000, 1500}) {
       for (int BT : {1, 7, 32, 36, 64, 256}) {
@@ -52,6 +52,15 @@ int main() {
                 }
               }
               if (cnt != kt.count()) fail("count", mode, t0, t1, BK, cnt);
+              // steady pairs of full items: consecutive visited tiles, whole, mask-free
+              for (int j = kt.next(0); j >= 0; j = kt.next(j + 1)) {
+                if (!kt.steady_pair(j)) continue;
+                ++steady;
+                for (int i = 1; i <= 5; ++i)
+                  if (kt.next(j + i) != j + i) fail("steady-next", mode, t0, t1, BK, j + i);
+                if ((j + 5) * BK > ke) fail("steady-whole", mode, t0, t1, BK, j);
+                if (kt.needs_mask(j + 1) || kt.needs_mask(j + 2)) fail("steady-mask", mode, t0, t1, BK, j);
+              }
               // the compile-time-mode instances walk the same tiles
               for (int t = 0; t <= kt.diag + 1; ++t) {
                 int a = -2, b = -2; bool ma = false, mb = false;
@@ -72,6 +81,6 @@ int main() {
       }
     }
   }
-  std::printf("%ld items checked, %d failures\n", checked, failures);
+  std::printf("%ld items checked, %ld steady pairs verified, %d failures\n", checked, steady, failures);
   return failures ? 1 : 0;
 }
