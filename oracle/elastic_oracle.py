@@ -45,6 +45,11 @@ What is computed (readings of points the summary leaves open are marked READING)
                      lse = log(e^a + e^b),  o = e^(a - lse) o_a + e^(b - lse) o_b.
     chunked_prefill  each query chunk attends every key up to its own end (the queries
                      are the last positions of the keys), chunk results concatenated.
+    block lists      READING (the survey's per-head block lists, the consumer half of
+                     content-based block selection): the key blocks query block qb of KV head
+                     g in sequence b may see are given explicitly, key blocks after qb are
+                     ignored (causal), and a query sees key j iff j <= i and j's block is
+                     listed for i's block.  An empty list leaves the row without keys.
     block_streaming  READING: the block-granular form of sink + window streaming is the
                      block pattern with block 64, ceil(sink / 64) sink blocks, a window of
                      window / 64 blocks that includes the query's own block, and no stride.
@@ -171,7 +176,50 @@ def allowed(i, j, full: bool, sparse: Optional[dict]) -> np.ndarray:
         if stride > 0:
             keep = keep | (kb % stride == 0)
         return causal & keep
+    if kind == "block_set":  # one (sequence, KV head) of a block-list pattern, resolved
+        B = sparse["block"]
+        vis = sparse["visible"]  # bool [query blocks, key blocks]
+        qb, kb = i // B, j // B
+        inside = (qb < vis.shape[0]) & (kb < vis.shape[1]) & (qb >= 0) & (kb >= 0)
+        got = np.zeros(np.broadcast(qb, kb).shape, dtype=bool)
+        qq, kk = np.broadcast_arrays(qb, kb)
+        got[inside] = vis[qq[inside], kk[inside]]
+        return causal & got
     raise ValueError(f"unknown sparse kind {kind!r}")
+
+
+def block_list_resolve(sparse: dict, b: int, g: int, n_kv_heads: int) -> dict:
+    """The block set of sequence b, KV head g from a block-list pattern:
+    {"kind": "block_list", "block": B, "row_ptr": [B*Hkv*nqb + 1], "col_idx": [...], "qblocks": nqb}
+    (CSR rows r = (b * Hkv + g) * nqb + qb, key block indices per row)."""
+    nqb = int(sparse["qblocks"])
+    rp = np.asarray(sparse["row_ptr"], dtype=np.int64)
+    ci = np.asarray(sparse["col_idx"], dtype=np.int64)
+    vis = np.zeros((nqb, nqb), dtype=bool)
+    for qb in range(nqb):
+        r = (b * n_kv_heads + g) * nqb + qb
+        kb = ci[rp[r]:rp[r + 1]]
+        kb = kb[(kb >= 0) & (kb <= qb)]   # later blocks are ignored (causal)
+        vis[qb, kb] = True
+    return {"kind": "block_set", "block": int(sparse["block"]), "visible": vis}
+
+
+def block_list_from_pattern(pattern: dict, batch: int, n_kv_heads: int, n_max: int) -> dict:
+    """The block lists that reproduce a fixed block pattern (every sequence and head alike)."""
+    B = pattern["block"]
+    nqb = -(-n_max // B)
+    rows = []
+    for qb in range(nqb):
+        i = qb * B + B - 1
+        kb = np.arange(qb + 1)
+        keep = allowed(np.full(qb + 1, i), kb * B, False, pattern)
+        rows.append(kb[keep])
+    row_ptr, col = [0], []
+    for _ in range(batch * n_kv_heads):
+        for r in rows:
+            col.extend(int(x) for x in r)
+            row_ptr.append(len(col))
+    return {"kind": "block_list", "block": B, "qblocks": nqb, "row_ptr": row_ptr, "col_idx": col}
 
 
 def row_key_counts(n: int, full: bool, sparse: Optional[dict], rows=None,
@@ -197,10 +245,15 @@ def entries(seqlens, head_mask, sparse, n_q_heads: int, n_kv_heads: int) -> int:
     """Allowed (query, key) pairs summed over all query heads and sequences."""
     G = n_q_heads // n_kv_heads
     modes = head_modes(head_mask, len(seqlens), n_kv_heads)
+    lists = sparse is not None and sparse.get("kind") == "block_list"
     cache = {}
     total = 0
     for b, n in enumerate(seqlens):
         for g in range(n_kv_heads):
+            if lists and not modes[b, g]:
+                sp = block_list_resolve(sparse, b, g, n_kv_heads)
+                total += G * int(row_key_counts(int(n), False, sp).sum())
+                continue
             key = (int(n), bool(modes[b, g]))
             if key not in cache:
                 cache[key] = int(row_key_counts(int(n), key[1], sparse).sum())
@@ -230,18 +283,24 @@ def effective_sparsity(seqlens, head_mask, sparse, n_q_heads, n_kv_heads) -> flo
 
 # ----------------------------------------------------------------------------- attention
 def _attend_block(Q, K, V, ii, full, sparse, scale):
-    """Rows ``ii`` (local positions) of one query head: exact two-pass softmax."""
+    """Rows ``ii`` (local positions) of one query head: exact two-pass softmax.  A row with
+    no allowed key (possible only with explicit block lists) gets o = 0, lse = -inf."""
     jj = np.arange(int(ii.max()) + 1)
     A = allowed(ii[:, None], jj[None, :], full, sparse)
     cols = np.nonzero(A.any(axis=0))[0]
+    o = np.zeros((len(ii), V.shape[1]))
+    lse = np.full(len(ii), -np.inf)
+    if len(cols) == 0:
+        return o, lse
     A = A[:, cols]
     s = scale * (Q[ii] @ K[cols].T)
     s = np.where(A, s, -np.inf)
-    m = s.max(axis=1, keepdims=True)
+    has = A.any(axis=1)
+    m = np.where(has, s.max(axis=1), 0.0)[:, None]
     p = np.exp(s - m)                      # exp(-inf) = 0 for disallowed keys
     denom = p.sum(axis=1, keepdims=True)
-    o = (p @ V[cols]) / denom
-    lse = m[:, 0] + np.log(denom[:, 0])
+    o[has] = (p[has] @ V[cols]) / denom[has]
+    lse[has] = m[has, 0] + np.log(denom[has, 0])
     return o, lse
 
 
@@ -284,7 +343,8 @@ def attention(q, k, v, cu_seqlens, head_mask, sparse, scale: Optional[float] = N
         Q = Qa[lo:hi_tok, h, :]
         K = Ka[lo:hi_tok, g, :]
         V = Va[lo:hi_tok, g, :]
-        ob, lb = _attend_block(Q, K, V, rows[sel] - lo, bool(modes[b, g]), sparse, scale)
+        sp = block_list_resolve(sparse, b, g, Hkv) if sparse is not None and sparse.get("kind") == "block_list" else sparse
+        ob, lb = _attend_block(Q, K, V, rows[sel] - lo, bool(modes[b, g]), sp, scale)
         o[sel, hi, :] = ob
         lse[hi, sel] = lb
 
@@ -357,8 +417,10 @@ def attention_kv(q, k, v, cu_q, cu_k, head_mask, sparse, scale: Optional[float] 
             V = Va[ck[b]:ck[b + 1], g, :]
             for r0 in range(0, nq, block_rows):
                 t = np.arange(r0, min(nq, r0 + block_rows))
+                sp = (block_list_resolve(sparse, b, g, Hkv)
+                      if sparse is not None and sparse.get("kind") == "block_list" else sparse)
                 ob, lb = _attend_block_abs(Qa[cq[b] + t, h, :], K, V, qp + t, pj,
-                                           bool(modes[b, g]), sparse, scale)
+                                           bool(modes[b, g]), sp, scale)
                 o[cq[b] + t, hi, :] = ob
                 lse[hi, cq[b] + t] = lb
     return o, lse
