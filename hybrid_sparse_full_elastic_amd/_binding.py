@@ -14,7 +14,7 @@ ABI_VERSION = 2
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
 BF16, FP32 = 0, 1
-STREAMING, BLOCK = 0, 1
+STREAMING, BLOCK, BLOCK_LIST = 0, 1, 2
 
 
 class ElasticError(RuntimeError):
@@ -29,7 +29,9 @@ class ElasticError(RuntimeError):
 class SparseCfg(C.Structure):
     _fields_ = [("kind", C.c_int32), ("sink_tokens", C.c_int32), ("window_tokens", C.c_int32),
                 ("block_size", C.c_int32), ("sink_blocks", C.c_int32),
-                ("local_blocks", C.c_int32), ("stride_blocks", C.c_int32)]
+                ("local_blocks", C.c_int32), ("stride_blocks", C.c_int32),
+                ("list_qblocks", C.c_int32), ("list_row_ptr", C.c_void_p),
+                ("list_col_idx", C.c_void_p)]
 
 
 def _load():
@@ -82,7 +84,45 @@ def sparse_cfg(d: Optional[dict]) -> Optional[SparseCfg]:
     if d["kind"] == "block":
         return SparseCfg(BLOCK, 0, 0, int(d["block"]), int(d["sink_blocks"]),
                          int(d["local_blocks"]), int(d["stride_blocks"]))
+    if d["kind"] == "block_list":
+        # CSR of key-block indices on the device; the struct keeps the tensors alive
+        rp, ci = d["row_ptr"], d["col_idx"]
+        for name, t in (("row_ptr", rp), ("col_idx", ci)):
+            if not (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == torch.int32 and t.is_contiguous()):
+                raise ValueError(f"block_list {name} must be a contiguous int32 device tensor")
+        cfg = SparseCfg(BLOCK_LIST, 0, 0, int(d["block"]), 0, 0, 0, int(d["qblocks"]),
+                        rp.data_ptr(), ci.data_ptr() if ci.numel() > 0 else rp.data_ptr())
+        cfg._keep = (rp, ci)
+        return cfg
     raise ValueError(f"unknown sparse kind {d['kind']!r}")
+
+
+def block_list_entries(seqlens, head_mask, n_q_heads: int, n_kv_heads: int, lists: dict) -> int:
+    """Allowed score entries for a block-list pattern, counted on the host from the CSR (the
+    library's counter cannot read device lists).  Full heads count n(n+1)/2 each."""
+    import numpy as np
+    B = int(lists["block"])
+    nqb = int(lists["qblocks"])
+    rp = lists["row_ptr"].cpu().numpy() if isinstance(lists["row_ptr"], torch.Tensor) else np.asarray(lists["row_ptr"])
+    ci = lists["col_idx"].cpu().numpy() if isinstance(lists["col_idx"], torch.Tensor) else np.asarray(lists["col_idx"])
+    G = n_q_heads // n_kv_heads
+    total = 0
+    for b, n in enumerate(int(x) for x in seqlens):
+        for g in range(n_kv_heads):
+            full = head_mask is None or int(np.asarray(head_mask)[b][g]) != 0
+            if full:
+                total += G * n * (n + 1) // 2
+                continue
+            for qb in range(-(-n // B)):
+                r = (b * n_kv_heads + g) * nqb + qb
+                kbs = np.unique(ci[rp[r]:rp[r + 1]])
+                kbs = kbs[(kbs >= 0) & (kbs <= qb)]
+                rows = min(n, qb * B + B) - qb * B       # query rows of this block
+                below = int((kbs < qb).sum())
+                total += G * rows * below * B
+                if (kbs == qb).any():                     # causal diagonal block
+                    total += G * rows * (rows + 1) // 2
+    return total
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -271,6 +311,8 @@ def lse_merge(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b: 
 
 def attn_entries(seqlens, head_mask, n_q_heads: int, n_kv_heads: int, sparse=None) -> int:
     """Allowed score entries over all query heads (host closed forms, no GPU involved)."""
+    if isinstance(sparse, dict) and sparse.get("kind") == "block_list":
+        return block_list_entries(seqlens, head_mask, n_q_heads, n_kv_heads, sparse)
     lens = (C.c_int32 * len(seqlens))(*[int(x) for x in seqlens])
     mask_arr = None
     if head_mask is not None:

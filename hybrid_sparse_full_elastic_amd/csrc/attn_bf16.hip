@@ -77,6 +77,17 @@ __device__ inline float max3f(float a, float b, float c) {
   return r;
 }
 
+// An empty statement that takes the values in registers: the computations producing them stay
+// above it.
+__device__ __forceinline__ void keep_here(const bf16x8 (&p)[2][2], const float (&l)[4]) {
+  asm volatile("" ::"v"(p[0][0]), "v"(p[0][1]), "v"(p[1][0]), "v"(p[1][1]), "v"(l[0]), "v"(l[1]),
+               "v"(l[2]), "v"(l[3]));
+}
+__device__ __forceinline__ void lds_wait_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding)
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | 0x70 | 0xF00 | ((((n) >> 4) & 3) << 14))
 
@@ -99,10 +110,11 @@ __device__ __host__ constexpr int v_swizzle(int row) {
   return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
-// One work item with its mode known at compile time.
-template <int D, int MODE>
+// One work item with its mode known at compile time.  KIND is the sparse kind of the launch:
+// each kernel instantiates its own copies of the item loops.
+template <int D, int MODE, int KIND>
 __device__ __forceinline__ void attn_item(
-    const WorkItem& it, LdsTiles<D>& lds, const uint16_t* __restrict__ q,
+    const WorkItem& it, LdsTiles<D>& lds, uint32_t* list_vis, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
     float* __restrict__ lse, const SeqGeom& geo, int Hq, int Hkv, int G, int BT, float scale_log2,
     const Pattern& pat) {
@@ -124,7 +136,14 @@ __device__ __forceinline__ void attn_item(
   const int t1 = min(t0 + BT, n) - 1;
   const int g = it.group;
   const int k_end = geo.k_pos + sp.nk;  // one past the last key (absolute)
-  const KeyTilesT<MODE> tiles(MODE, pat, sp.qp + t0, sp.qp + t1, BK, geo.k_pos, k_end);
+  // the item's key tiles: closed forms, or the block lists marked in LDS (whole workgroup)
+  const auto tiles = [&] {
+    if constexpr (MODE == MODE_LIST)
+      return list_tiles(list_vis, pat, it.seq, g, Hkv, sp.qp + t0, sp.qp + t1, geo.k_pos, k_end, BK,
+                        (int)threadIdx.x, NT);
+    else
+      return KeyTilesT<MODE>(MODE, pat, sp.qp + t0, sp.qp + t1, BK, geo.k_pos, k_end);
+  }();
   const int blk_shift = 31 - __clz(pat.block);  // block sizes are powers of two
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -232,6 +251,8 @@ __device__ __forceinline__ void attn_item(
       const bool vis = kblk < pat.sink_blocks || qblk - kblk <= pat.local_blocks ||
                        (pat.stride_blocks > 0 && kblk % pat.stride_blocks == 0);
       b = vis ? 0 : 0x7fffffff;
+    } else if (MODE == MODE_LIST) {
+      b = tiles.lists(kt, qblk) ? 0 : 0x7fffffff;
     }
     const int base = kt * BK + half * 4;
 #pragma unroll
@@ -362,8 +383,7 @@ __device__ __forceinline__ void attn_item(
         }
       }
       // keep tile j's weights in this region (no sinking past the mask branch)
-      asm volatile("" ::"v"(pop[0][0]), "v"(pop[0][1]), "v"(pop[1][0]), "v"(pop[1][1]), "v"(ls[0]),
-                   "v"(ls[1]), "v"(ls[2]), "v"(ls[3]));
+      keep_here(pop, ls);
       if (!STEADY && has_next && tiles.needs_mask(kt_n1)) apply_mask(sn, kt_n1);
       // Region 2: P.V of tile j (NPV MFMAs; transposing V reads two fragments ahead) with the
       // maximum of tile j+1 placed between them.
@@ -419,7 +439,7 @@ __device__ __forceinline__ void attn_item(
       else WAIT_VMCNT(0);
       // LDS reads of this step done, then the barrier.  (__syncthreads would also wait for the
       // DMA issued this step, which must stay in flight.)
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      lds_wait_barrier();
       kt_cur = kt_n1;
       kt_n1 = kt_n2;
       kt_n2 = kt_n3;
@@ -462,7 +482,7 @@ __device__ __forceinline__ void attn_item(
       *reinterpret_cast<u32x2*>(stage + l32 * D + ((chunk ^ k_swizzle<D>(l32)) * 8) + half * 4) =
           __builtin_bit_cast(u32x2, w);
     }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave reads back its own rows
+  lds_wait();  // the wave reads back its own rows
   constexpr int RPI = 64 / CPR;                        // rows per store instruction
 #pragma unroll
   for (int i = 0; i < 32 / RPI; ++i) {
@@ -477,25 +497,29 @@ __device__ __forceinline__ void attn_item(
     lse[(int64_t)qhead * geo.total_q + seq0 + qi] = (m_sc + __log2f(lt)) * LN2;
 }
 
-template <int D>
+// One kernel per sparse pattern kind: every launch holds full items and items of one sparse
+// kind, so each instantiation carries two item loops only (less code and fewer live scalar
+// registers than one kernel for every mode).
+template <int D, int KIND>
 __global__ __launch_bounds__(BF16_NW * 64, 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, SeqGeom geo, int Hq, int Hkv, int G, int BT,
     float scale_log2, const int32_t* __restrict__ head_mask, Pattern pat,
     const WorkItem* __restrict__ items, const int32_t* __restrict__ n_items) {
+  constexpr bool LISTS = KIND == ELASTIC_SPARSE_BLOCK_LIST;
   __shared__ __attribute__((aligned(1024))) LdsTiles<D> lds;
+  __shared__ uint32_t list_vis[LISTS ? LIST_MAX_KB : 1];  // block lists: visibility per key block
   if ((int)blockIdx.x >= *n_items) return;
   const WorkItem it = items[blockIdx.x];
   const bool full = head_mask == nullptr || head_mask[it.seq * Hkv + it.group] != 0;
   if (full)
-    attn_item<D, MODE_FULL>(it, lds, q, k, v, o, lse, geo, Hq, Hkv, G, BT,
-                            scale_log2, pat);
-  else if (pat.kind == ELASTIC_SPARSE_STREAMING)
-    attn_item<D, MODE_STREAM>(it, lds, q, k, v, o, lse, geo, Hq, Hkv, G, BT,
-                              scale_log2, pat);
+    attn_item<D, MODE_FULL, KIND>(it, lds, list_vis, q, k, v, o, lse, geo, Hq, Hkv, G, BT, scale_log2, pat);
+  else if constexpr (KIND == ELASTIC_SPARSE_STREAMING)
+    attn_item<D, MODE_STREAM, KIND>(it, lds, list_vis, q, k, v, o, lse, geo, Hq, Hkv, G, BT, scale_log2, pat);
+  else if constexpr (KIND == ELASTIC_SPARSE_BLOCK)
+    attn_item<D, MODE_BLOCK, KIND>(it, lds, list_vis, q, k, v, o, lse, geo, Hq, Hkv, G, BT, scale_log2, pat);
   else
-    attn_item<D, MODE_BLOCK>(it, lds, q, k, v, o, lse, geo, Hq, Hkv, G, BT,
-                             scale_log2, pat);
+    attn_item<D, MODE_LIST, KIND>(it, lds, list_vis, q, k, v, o, lse, geo, Hq, Hkv, G, BT, scale_log2, pat);
 }
 
 }  // namespace
@@ -508,14 +532,22 @@ hipError_t launch_attn_bf16(int head_dim, const void* q, const void* k, const vo
   const float scale_log2 = scale * 1.4426950408889634f;
   const int G = n_q_heads / n_kv_heads;
   if (grid <= 0) return hipSuccess;
-  if (head_dim == 128)
-    hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3((unsigned)grid), dim3(BF16_NW * 64), 0, stream,
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(BF16_NW * 64), 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
                        geo, n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask, pat, items, n_items);
-  else
-    hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3((unsigned)grid), dim3(BF16_NW * 64), 0, stream,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
-                       geo, n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask, pat, items, n_items);
+  };
+  // without a head mask every item is full: any instantiation serves
+  const int kind = head_mask == nullptr ? ELASTIC_SPARSE_STREAMING : pat.kind;
+  if (head_dim == 128) {
+    if (kind == ELASTIC_SPARSE_STREAMING) launch(attn_bf16_kernel<128, ELASTIC_SPARSE_STREAMING>);
+    else if (kind == ELASTIC_SPARSE_BLOCK) launch(attn_bf16_kernel<128, ELASTIC_SPARSE_BLOCK>);
+    else launch(attn_bf16_kernel<128, ELASTIC_SPARSE_BLOCK_LIST>);
+  } else {
+    if (kind == ELASTIC_SPARSE_STREAMING) launch(attn_bf16_kernel<64, ELASTIC_SPARSE_STREAMING>);
+    else if (kind == ELASTIC_SPARSE_BLOCK) launch(attn_bf16_kernel<64, ELASTIC_SPARSE_BLOCK>);
+    else launch(attn_bf16_kernel<64, ELASTIC_SPARSE_BLOCK_LIST>);
+  }
   return hipGetLastError();
 }
 

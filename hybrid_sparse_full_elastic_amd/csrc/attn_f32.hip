@@ -7,6 +7,8 @@
 // workgroup's rows are the G heads of BT tokens, so every K/V tile staged in LDS is read by
 // all G heads of the group with broadcast (conflict-free) LDS reads.  Scores of a 32-key
 // tile are formed first, then one online-softmax update per tile (exp2 domain).
+#include <type_traits>
+
 #include "elastic_internal.hpp"
 
 namespace elastic {
@@ -24,6 +26,7 @@ __global__ __launch_bounds__(F32_ROWS, 1) void attn_f32_kernel(
   constexpr int CH = BK * D / 4;  // float4 chunks per tile
   __shared__ __attribute__((aligned(16))) float k_lds[BK * D];
   __shared__ __attribute__((aligned(16))) float v_lds[BK * D];
+  __shared__ uint32_t list_vis[LIST_MAX_KB];  // block lists: visibility of each key block
 
   if ((int)blockIdx.x >= *n_items) return;
   const WorkItem it = items[blockIdx.x];
@@ -37,7 +40,6 @@ __global__ __launch_bounds__(F32_ROWS, 1) void attn_f32_kernel(
   const bool full = head_mask == nullptr || head_mask[it.seq * Hkv + g] != 0;
   const int mode = full ? MODE_FULL : pat.kind;
   const int k_end = geo.k_pos + sp.nk;
-  const KeyTiles tiles(mode, pat, sp.qp + t0, sp.qp + t1, BK, geo.k_pos, k_end);
 
   const int tid = threadIdx.x;
   const int tl = tid / G, hh = tid - (tid / G) * G;
@@ -63,6 +65,18 @@ __global__ __launch_bounds__(F32_ROWS, 1) void attn_f32_kernel(
   for (int d = 0; d < D; ++d) acc[d] = 0.f;
   float m_run = -1.0e30f, l_run = 0.f;
 
+  const int blk_shift = 31 - __clz(pat.block);  // block sizes are powers of two
+  // key tiles: closed forms, or the block lists marked in LDS (one loop for both)
+  const bool LIST = mode == MODE_LIST;
+  struct {
+    bool list;
+    KeyTiles kt;
+    ListTiles lt;
+    __device__ int next(int x) const { return list ? lt.next(x) : kt.next(x); }
+    __device__ bool needs_mask(int x) const { return list ? lt.needs_mask(x) : kt.needs_mask(x); }
+  } tiles{LIST, KeyTiles(LIST ? MODE_FULL : mode, pat, sp.qp + t0, sp.qp + t1, BK, geo.k_pos, k_end),
+          LIST ? list_tiles(list_vis, pat, it.seq, g, Hkv, sp.qp + t0, sp.qp + t1, geo.k_pos, k_end, BK, tid, NT)
+               : ListTiles{}};
   for (int kt = tiles.next(0); kt >= 0; kt = tiles.next(kt + 1)) {
     __syncthreads();  // previous tile fully consumed
     for (int c = tid; c < CH; c += NT) {
@@ -80,6 +94,11 @@ __global__ __launch_bounds__(F32_ROWS, 1) void attn_f32_kernel(
     __syncthreads();
 
     const bool masked = tiles.needs_mask(kt);
+    bool row_sees_block = true;  // block lists: does this row's query block list the tile's block?
+    if (LIST) {
+      const int bit = (qabs >> blk_shift) - tiles.lt.qb0;
+      row_sees_block = bit >= 0 && bit < LIST_MAX_QB && ((tiles.lt.vis_of(kt) >> bit) & 1u);
+    }
     float s[BK];
     float mt = -__builtin_huge_valf();
 #pragma unroll
@@ -89,7 +108,8 @@ __global__ __launch_bounds__(F32_ROWS, 1) void attn_f32_kernel(
       for (int d = 0; d < D; ++d) dot = fmaf(qr[d], k_lds[j * D + d], dot);
       float x = dot * scale_log2;
       const int kj = kt * BK + j;
-      if (masked && (!valid || kj >= k_end || !key_allowed(mode, pat, qabs, kj))) x = -__builtin_huge_valf();
+      const bool ok = LIST ? (row_sees_block && kj <= qabs) : key_allowed(mode, pat, qabs, kj);
+      if (masked && (!valid || kj >= k_end || !ok)) x = -__builtin_huge_valf();
       s[j] = x;
       mt = fmaxf(mt, x);
     }

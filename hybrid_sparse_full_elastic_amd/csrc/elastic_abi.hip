@@ -71,7 +71,22 @@ int check_pattern(const elastic_sparse_cfg* s) {
     if (s->block_size != 64 && s->block_size != 128) return ELASTIC_EUNSUPPORTED;
     return ELASTIC_OK;
   }
+  if (s->kind == ELASTIC_SPARSE_BLOCK_LIST) {
+    if (s->list_qblocks < 1 || s->list_row_ptr == nullptr || s->list_col_idx == nullptr)
+      return ELASTIC_EINVAL;
+    if (s->block_size != 64 && s->block_size != 128) return ELASTIC_EUNSUPPORTED;
+    return ELASTIC_OK;
+  }
   return ELASTIC_EINVAL;
+}
+
+// Block lists: the CSR must hold a row for every query block the call reaches, and one item's
+// key blocks must fit the kernels' LDS visibility words.
+int check_lists(const elastic_sparse_cfg* s, int64_t max_q_pos, int64_t max_k) {
+  if (s == nullptr || s->kind != ELASTIC_SPARSE_BLOCK_LIST) return ELASTIC_OK;
+  if (max_q_pos >= 0 && max_q_pos / s->block_size >= s->list_qblocks) return ELASTIC_EINVAL;
+  if ((max_k + s->block_size - 1) / s->block_size + 1 > LIST_MAX_KB) return ELASTIC_EUNSUPPORTED;
+  return ELASTIC_OK;
 }
 
 Pattern to_pattern(const elastic_sparse_cfg* s) {
@@ -89,6 +104,9 @@ Pattern to_pattern(const elastic_sparse_cfg* s) {
   p.sink_blocks = s->sink_blocks;
   p.local_blocks = s->local_blocks;
   p.stride_blocks = s->stride_blocks;
+  p.qblocks = s->kind == ELASTIC_SPARSE_BLOCK_LIST ? s->list_qblocks : 0;
+  p.row_ptr = s->kind == ELASTIC_SPARSE_BLOCK_LIST ? s->list_row_ptr : nullptr;
+  p.col_idx = s->kind == ELASTIC_SPARSE_BLOCK_LIST ? s->list_col_idx : nullptr;
   return p;
 }
 
@@ -209,7 +227,11 @@ int attn_call(const char* who, const void* q, const void* k, const void* v, void
   if (sparse != nullptr) {
     const int st = check_pattern(sparse);
     if (st != ELASTIC_OK) return st;
-    if (sparse->kind == ELASTIC_SPARSE_BLOCK && k_pos % sparse->block_size != 0) return ELASTIC_EINVAL;
+    if (sparse->kind != ELASTIC_SPARSE_STREAMING && k_pos % sparse->block_size != 0) return ELASTIC_EINVAL;
+    // last query position any sequence can reach: q_pos + max_q - 1, or k_pos + max_k - 1
+    const int64_t max_q_pos = q_pos >= 0 ? (int64_t)q_pos + max_q - 1 : (int64_t)k_pos + max_k - 1;
+    const int lst = check_lists(sparse, max_q_pos, max_k);
+    if (lst != ELASTIC_OK) return lst;
   }
   if (dtype != ELASTIC_BF16 && dtype != ELASTIC_FP32) return ELASTIC_EUNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return ELASTIC_EUNSUPPORTED;
@@ -313,6 +335,7 @@ int elastic_attn_entries(const int32_t* seqlens_host, int32_t batch,
     int64_t full_e = -1, sparse_e = -1;
     for (int32_t g = 0; g < n_kv_heads; ++g) {
       const bool full = head_mask_host == nullptr || head_mask_host[(int64_t)b * n_kv_heads + g] != 0;
+      if (!full && sparse->kind == ELASTIC_SPARSE_BLOCK_LIST) return ELASTIC_EUNSUPPORTED;
       int64_t& slot = full ? full_e : sparse_e;
       if (slot < 0) slot = head_entries(seqlens_host[b], full, sparse);
       total += G * slot;

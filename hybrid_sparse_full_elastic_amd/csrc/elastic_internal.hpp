@@ -15,14 +15,109 @@
 
 namespace elastic {
 
-enum : int { MODE_STREAM = ELASTIC_SPARSE_STREAMING, MODE_BLOCK = ELASTIC_SPARSE_BLOCK, MODE_FULL = 2 };
+enum : int {
+  MODE_STREAM = ELASTIC_SPARSE_STREAMING,
+  MODE_BLOCK = ELASTIC_SPARSE_BLOCK,
+  MODE_LIST = ELASTIC_SPARSE_BLOCK_LIST,
+  MODE_FULL = 3
+};
 
 // Sparse pattern as the kernels see it (by value in kernel arguments).
 struct Pattern {
   int kind;                  // ELASTIC_SPARSE_*
   int sink, window;          // streaming
   int block, sink_blocks, local_blocks, stride_blocks;
+  int qblocks;               // block list: CSR rows per (sequence, KV head)
+  const int32_t* row_ptr;    // block list (device)
+  const int32_t* col_idx;
 };
+
+// Block lists: the key blocks an item may visit are marked in LDS, one word per key block
+// (bit i = visible to the item's (i+1)-th query block); LIST_MAX_KB words per workgroup.
+constexpr int LIST_MAX_KB = 4096;
+constexpr int LIST_MAX_QB = 8;  // query blocks one item may span
+
+// Key tiles of one block-list item, read from the LDS visibility words vis[kb - kb0].  Same
+// interface as KeyTilesT; every call is made by the whole workgroup with uniform arguments.
+struct ListTiles {
+  int BK, tpb, t0, t1, lo, last, k_end, qb0, kb0, kb_last;
+  unsigned full_mask;  // every query block of the item
+  const uint32_t* vis;
+
+  __device__ unsigned vis_of(int kt) const { return vis[kt / tpb - kb0]; }
+
+  // Does the list of query block qblk (absolute) hold the key block of tile kt?
+  __device__ bool lists(int kt, int qblk) const {
+    const int bit = qblk - qb0;
+    return bit >= 0 && bit < LIST_MAX_QB && ((vis_of(kt) >> bit) & 1u);
+  }
+
+  __device__ int next(int kt) const {
+    if (kt < lo) kt = lo;
+    if (kt > last) return -1;
+    const int kb = kt / tpb;
+    if (vis[kb - kb0] != 0) return kt;
+    const int lane = __lane_id();
+    for (int base = kb + 1; base <= kb_last; base += 64) {
+      const int b = base + lane;
+      const uint64_t m = __ballot(b <= kb_last && vis[b - kb0] != 0);
+      if (m != 0) {
+        const int t = (base + __ffsll((unsigned long long)m) - 1) * tpb;
+        return t <= last ? t : -1;
+      }
+    }
+    return -1;
+  }
+
+  __device__ bool needs_mask(int kt) const {
+    const int k0 = kt * BK, k1 = k0 + BK - 1;
+    return k1 > t0 || k1 >= k_end || vis_of(kt) != full_mask;
+  }
+
+  __device__ bool steady_pair(int) const { return false; }
+};
+
+// Builds the ListTiles of one block-list item: marks in vis the key blocks of the range that
+// the item's query blocks list (ignoring blocks after the query block), then returns the
+// walker.  The whole workgroup calls it (two barriers).  a0, a1: absolute positions of the
+// item's first and last query; [k_begin, k_end): its key range.
+__device__ inline ListTiles list_tiles(uint32_t* vis, const Pattern& p, int b, int g,
+                                       int n_kv_heads, int a0, int a1, int k_begin, int k_end,
+                                       int BK, int tid, int nt) {
+  ListTiles t;
+  t.BK = BK;
+  t.tpb = p.block / BK;
+  t.t0 = a0;
+  t.t1 = a1;
+  t.k_end = k_end;
+  t.vis = vis;
+  t.lo = k_begin / BK;
+  t.kb0 = k_begin / p.block;
+  const int qb0 = a0 > 0 ? a0 / p.block : 0;
+  const int qb1 = a1 >= 0 ? a1 / p.block : -1;
+  t.qb0 = qb0;
+  const int kb_end = k_end > k_begin ? (k_end - 1) / p.block : t.kb0 - 1;
+  t.kb_last = qb1 < kb_end ? qb1 : kb_end;
+  const int diag = a1 >= 0 ? a1 / BK : -1;
+  const int hi = k_end > k_begin ? (k_end - 1) / BK : t.lo - 1;
+  t.last = diag < hi ? diag : hi;
+  if (t.kb_last - t.kb0 + 1 > LIST_MAX_KB) t.kb_last = t.kb0 + LIST_MAX_KB - 1;  // checked on the host
+  const int nqb = qb1 - qb0 + 1;
+  t.full_mask = nqb >= 32 ? 0xffffffffu : (1u << (nqb > 0 ? nqb : 0)) - 1u;
+  for (int i = tid; i <= t.kb_last - t.kb0; i += nt) vis[i] = 0;
+  __syncthreads();
+  for (int qb = qb0; qb <= qb1 && qb - qb0 < LIST_MAX_QB; ++qb) {
+    if (qb >= p.qblocks) break;
+    const int64_t r = ((int64_t)b * n_kv_heads + g) * p.qblocks + qb;
+    const int e0 = p.row_ptr[r], e1 = p.row_ptr[r + 1];
+    for (int e = e0 + tid; e < e1; e += nt) {
+      const int kb = p.col_idx[e];
+      if (kb >= t.kb0 && kb <= t.kb_last && kb <= qb) atomicOr(&vis[kb - t.kb0], 1u << (qb - qb0));
+    }
+  }
+  __syncthreads();
+  return t;
+}
 
 // Query/key geometry of one attention call.  Sequence b has queries at rows
 // [cu_q[b], cu_q[b+1]) of q/o and keys at rows [cu_k[b], cu_k[b+1]) of k/v (a null array
@@ -110,6 +205,9 @@ struct KeyTilesT {
       qb1 = t1 / p.block;
     }
   }
+
+  // Block lists only (ListTiles): closed-form patterns have no lists.
+  __host__ __device__ bool lists(int, int) const { return true; }
 
   // Smallest key block >= kb that some query block in [qb0, qb1] may see.
   __host__ __device__ int next_block(int kb) const {

@@ -111,11 +111,23 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     const int t1 = min(t0 + BT, n) - 1;
     const int mi = b * n_kv_heads + g;
     const bool full = mask_cached ? s_full[mi] != 0 : (head_mask == nullptr || head_mask[mi] != 0);
-    const KeyTiles kt(full ? MODE_FULL : pat.kind, pat, qp + t0, qp + t1, BK, geo.k_pos, geo.k_pos + nk);
     it.seq = b;
     it.group = g;
     it.qtile = qt;
-    it.cost = kt.count();
+    if (!full && pat.kind == ELASTIC_SPARSE_BLOCK_LIST) {
+      // block lists: listed blocks of the item's query blocks (an upper bound of the union)
+      const int a0 = qp + t0, a1 = qp + t1;
+      int c = 0;
+      if (a1 >= 0)
+        for (int qb = a0 > 0 ? a0 / pat.block : 0; qb <= a1 / pat.block && qb < pat.qblocks; ++qb) {
+          const int64_t r = ((int64_t)b * n_kv_heads + g) * pat.qblocks + qb;
+          c += pat.row_ptr[r + 1] - pat.row_ptr[r];
+        }
+      it.cost = c * (pat.block / BK);
+    } else {
+      const KeyTiles kt(full ? MODE_FULL : pat.kind, pat, qp + t0, qp + t1, BK, geo.k_pos, geo.k_pos + nk);
+      it.cost = kt.count();
+    }
   };
   for (int u = tid; u < nitem; u += PLAN_THREADS) {
     WorkItem it;

@@ -61,18 +61,32 @@ enum elastic_sparse_kind {
    * kb < sink_blocks, or qb - kb <= local_blocks, or (stride_blocks > 0 and
    * kb % stride_blocks == 0).  Blocks strictly below the diagonal are fully visible; the
    * diagonal block is causal inside. */
-  ELASTIC_SPARSE_BLOCK = 1
+  ELASTIC_SPARSE_BLOCK = 1,
+  /* Explicit block lists per sequence and key/value head, the consumer side of a
+   * content-based block selection (summary section 4 and appendix G.2 name XAttention's
+   * block selection).  For sequence b, KV head g and query block qb = i / block_size, CSR
+   * row r = (b * n_kv_heads + g) * list_qblocks + qb lists the key blocks
+   * list_col_idx[list_row_ptr[r] .. list_row_ptr[r+1]); query i sees key j <= i iff
+   * j / block_size is listed.  Listed blocks after qb are ignored; a query block with an
+   * empty list leaves its rows without keys (o = 0, lse = -inf). */
+  ELASTIC_SPARSE_BLOCK_LIST = 2
 };
 
-/* Pattern of the sparse heads.  Read on the host during the call only. */
+/* Pattern of the sparse heads.  The struct is read on the host during the call; the block
+ * lists it points at are read by the kernels on the device. */
 typedef struct elastic_sparse_cfg {
   int32_t kind;          /* enum elastic_sparse_kind */
   int32_t sink_tokens;   /* streaming: >= 0 */
   int32_t window_tokens; /* streaming: >= 1 */
-  int32_t block_size;    /* block: 64 or 128 */
+  int32_t block_size;    /* block, block list: 64 or 128 */
   int32_t sink_blocks;   /* block: >= 0 */
   int32_t local_blocks;  /* block: >= 0 (blocks strictly before the diagonal block) */
   int32_t stride_blocks; /* block: >= 0, 0 = no strided blocks */
+  int32_t list_qblocks;  /* block list: CSR rows per (sequence, KV head), >= query blocks */
+  const int32_t* list_row_ptr; /* block list: device int32 [batch * n_kv_heads * list_qblocks + 1],
+                                  non-decreasing, list_row_ptr[0] = 0 */
+  const int32_t* list_col_idx; /* block list: device int32 key-block indices, each row ascending
+                                  without repeats */
 } elastic_sparse_cfg;
 
 /* ABI version compiled into the library (ELASTIC_ABI_VERSION). */
@@ -167,7 +181,9 @@ int elastic_attn_prefill(const void* q, const void* k, const void* v, void* o, i
  *  workspace   elastic_attn_workspace_size(dtype, batch, total_q, n_q_heads, n_kv_heads,
  *              head_dim) bytes.
  * Other arguments, supported shapes and errors as for elastic_attn_prefill;
- * ELASTIC_EINVAL also for a misaligned k_pos, q_pos < -1, or positions past 2^31 - 1.
+ * ELASTIC_EINVAL also for a misaligned k_pos, q_pos < -1, positions past 2^31 - 1, or block
+ * lists with fewer than (last query position / block_size + 1) rows per (sequence, head);
+ * ELASTIC_EUNSUPPORTED for block lists over more than 4095 key blocks.
  * elastic_attn_prefill is this call with q = k rows, q_pos = k_pos = 0.
  */
 int elastic_attn_prefill_kv(const void* q, const void* k, const void* v, void* o, int32_t dtype,
@@ -200,7 +216,8 @@ int elastic_lse_merge(const void* o_a, const float* lse_a, const void* o_b, cons
  * modes (host int32 [batch, n_kv_heads], NULL = all full).  Effective attention FLOPs are
  * 4 * head_dim * entries.  Closed forms: full n(n+1)/2 per head; streaming
  * c(c+1)/2 + (n-c)c with c = min(n, sink+window); block: per query block, the visible
- * earlier blocks times block_size plus the causal diagonal block.
+ * earlier blocks times block_size plus the causal diagonal block.  Block lists live on the
+ * device: a call with block-list sparse heads returns ELASTIC_EUNSUPPORTED.
  */
 int elastic_attn_entries(const int32_t* seqlens_host, int32_t batch,
                          const int32_t* head_mask_host, int32_t n_q_heads, int32_t n_kv_heads,

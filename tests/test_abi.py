@@ -181,3 +181,43 @@ def test_entry_counter_at_workload_sizes():
     assert ext.attn_entries([65536], [[0]], 1, 1, w.sparse) == 140239936
     w = syn.WORKLOADS["fp32-512-s4w64"]
     assert ext.attn_entries([512], [[1, 0]], 8, 2, w.sparse) == 4 * (512 * 513 // 2) + 4 * 32538
+
+
+def _lists(rows, B=64):
+    rp, ci = [0], []
+    for r in rows:
+        ci.extend(r)
+        rp.append(len(ci))
+    return {"kind": "block_list", "block": B, "qblocks": len(rows), "row_ptr": rp, "col_idx": ci}
+
+
+def test_block_list_entry_counter_matches_oracle():
+    """The binding's host counter for block lists (the library cannot read device lists)."""
+    rng = np.random.default_rng(5)
+    n, B, hkv = 300, 64, 2
+    nqb = -(-n // B)
+    rows = []
+    for _ in range(hkv):
+        for qb in range(nqb):
+            rows.append(sorted(set(rng.choice(nqb + 1, size=rng.integers(0, 4)).tolist())))
+    lists = _lists(rows, B)
+    mask = [[0, 1]]
+    assert ext.block_list_entries([n], mask, 8, hkv, lists) == oracle.entries([n], mask, lists, 8, hkv)
+    # the library's counter declines block lists with sparse heads
+    cfg = ext.SparseCfg(2, 0, 0, 64, 0, 0, 0, nqb, 0x1000, 0x1000)
+    lens = (C.c_int32 * 1)(n)
+    m = (C.c_int32 * 2)(0, 1)
+    out = C.c_int64(0)
+    assert L.elastic_attn_entries(lens, 1, m, 8, 2, C.byref(cfg), C.byref(out)) == 2
+
+
+def test_block_list_validation_without_gpu():
+    EINVAL, EUNS = 1, 2
+    assert _attn(sparse=ext.SparseCfg(2, 0, 0, 64, 0, 0, 0, 0, 0x1000, 0x1000), mask=FAKE) == EINVAL
+    assert _attn(sparse=ext.SparseCfg(2, 0, 0, 64, 0, 0, 0, 4, None, 0x1000), mask=FAKE) == EINVAL
+    assert _attn(sparse=ext.SparseCfg(2, 0, 0, 96, 0, 0, 0, 4, 0x1000, 0x1000), mask=FAKE) == EUNS
+    # T = 256 needs 4 query-block rows of 64 tokens: 3 are too few
+    assert _attn(sparse=ext.SparseCfg(2, 0, 0, 64, 0, 0, 0, 3, 0x1000, 0x1000), mask=FAKE) == EINVAL
+    # key ranges must start on a block of the list
+    assert _attn_kv(sparse=ext.SparseCfg(2, 0, 0, 128, 0, 0, 0, 16, 0x1000, 0x1000), mask=FAKE,
+                    kpos=64) == EINVAL
