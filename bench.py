@@ -191,12 +191,15 @@ def recorded_traffic(workload):
     summary, or None when the kernel source has changed since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"attn_bf16_kernel-{workload}.pmc.txt")
-    src = os.path.join(ROOT, "hybrid_sparse_full_elastic_amd", "csrc", "attn_bf16.hip")
+    csrc = os.path.join(ROOT, "hybrid_sparse_full_elastic_amd", "csrc")
     if not os.path.exists(path):
         return None
     fields = dict(line.split(": ", 1) for line in open(path).read().splitlines()
                   if line and not line.startswith("#") and ": " in line)
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in ("attn_bf16.hip", "elastic_internal.hpp"):  # the kernel and its tile walkers
+        h.update(open(os.path.join(csrc, name), "rb").read())
+    digest = h.hexdigest()[:16]
     if fields.get("attn_source_sha256_16") != digest:
         return None
     return int(float(fields["traffic_bytes_per_launch"]))
@@ -218,8 +221,9 @@ def _time_attn(ext, torch, stream, fn, reps=10, warm=3):
 def deployment(ext, torch, w, q, k, v, o, mask, ws, stream):
     """The pages' inference settings on the same 32K layer and router mask: prefill in chunks
     of 16,384 queries (each chunk over its whole prefix) against one launch, a key range
-    split in two and merged by LSE, the merge kernel's bandwidth, and block-granular
-    streaming (block 64, 128 sink tokens, window 1024) on every head."""
+    split in two and merged by LSE, the merge kernel's bandwidth, block-granular streaming
+    (block 64, 128 sink tokens, window 1024) on every head, and explicit per-head block lists."""
+    from synth import inputs as syn
     T, hq, D = q.shape
     hkv = k.shape[1]
     mask_h = mask.cpu().numpy()
@@ -254,6 +258,18 @@ def deployment(ext, torch, w, q, k, v, o, mask, ws, stream):
     ms_bs = _time_attn(ext, torch, stream, lambda: ext.attn_prefill(
         q, k, v, max_seqlen=T, head_mask=zeros, sparse=bstream, out=o, workspace=ws))
     ent_bs = ext.attn_entries([T], [[0] * hkv], hq, hkv, bstream)
+    # explicit per-head block lists shaped like a content-based selector's output (block 128:
+    # the first block, the diagonal and 8% of the earlier blocks), on every head and on the
+    # router's sparse heads
+    sel = syn.selection_lists(70, 1, hkv, T, 128, 0.08)
+    sel_dev = dict(sel, row_ptr=torch.from_numpy(sel["row_ptr"]).to(q.device),
+                   col_idx=torch.from_numpy(sel["col_idx"]).to(q.device))
+    ms_sel = _time_attn(ext, torch, stream, lambda: ext.attn_prefill(
+        q, k, v, max_seqlen=T, head_mask=zeros, sparse=sel_dev, out=o, workspace=ws))
+    ent_sel = ext.attn_entries([T], [[0] * hkv], hq, hkv, sel)
+    ms_selm = _time_attn(ext, torch, stream, lambda: ext.attn_prefill(
+        q, k, v, max_seqlen=T, head_mask=mask, sparse=sel_dev, out=o, workspace=ws))
+    ent_selm = ext.attn_entries([T], mask_h, hq, hkv, sel)
     return {"one_launch_ms": round(one, 4),
             "chunked_16384_ms": round(ms_chunk, 4),
             "chunked_tflops": round(4 * D * ent / ms_chunk / 1e9, 2),
@@ -261,7 +277,11 @@ def deployment(ext, torch, w, q, k, v, o, mask, ws, stream):
             "lse_merge_us": round(ms_merge * 1e3, 2),
             "lse_merge_gbs": round(merge_bytes / (ms_merge * 1e-3) / 1e9, 1),
             "block_streaming_b64_s128_w1024_ms": round(ms_bs, 4),
-            "block_streaming_tflops": round(4 * D * ent_bs / ms_bs / 1e9, 2)}
+            "block_streaming_tflops": round(4 * D * ent_bs / ms_bs / 1e9, 2),
+            "block_lists_sel8_all_heads_ms": round(ms_sel, 4),
+            "block_lists_sel8_all_heads_tflops": round(4 * D * ent_sel / ms_sel / 1e9, 2),
+            "block_lists_sel8_router_mask_ms": round(ms_selm, 4),
+            "block_lists_sel8_router_mask_tflops": round(4 * D * ent_selm / ms_selm / 1e9, 2)}
 
 
 def router_detail(ext, torch, hidden, w1, w2, cu, threshold, logits, mask, ws, stream, reps=10):

@@ -221,3 +221,23 @@ def spread_rows(seqlen: int, count: int, seed: int = 0) -> np.ndarray:
     rows = set(rng.choice(seqlen, size=min(count, seqlen), replace=False).tolist())
     rows.update({0, seqlen - 1})
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def selection_lists(seed: int, batch: int, n_kv_heads: int, seqlen: int, block: int,
+                    density: float, sink_blocks: int = 1) -> dict:
+    """Seeded block lists shaped like the output of a content-based block selector, in CSR
+    order (sequence, KV head, query block): for query block ``qb`` the first ``sink_blocks``
+    blocks, the block ``qb`` itself and each earlier block with probability ``density``.
+    The draw for row r uses ``default_rng([seed, 7, r])``."""
+    nqb = (seqlen + block - 1) // block
+    rp, ci = [0], []
+    for r in range(batch * n_kv_heads * nqb):
+        qb = r % nqb
+        rng = np.random.default_rng([seed, 7, r])
+        pick = rng.random(qb) < density
+        pick[:min(sink_blocks, qb)] = True
+        ci.extend(np.nonzero(pick)[0].tolist())
+        ci.append(qb)
+        rp.append(len(ci))
+    return {"kind": "block_list", "block": block, "qblocks": nqb,
+            "row_ptr": np.asarray(rp, dtype=np.int32), "col_idx": np.asarray(ci, dtype=np.int32)}
