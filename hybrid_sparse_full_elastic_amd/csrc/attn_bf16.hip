@@ -88,6 +88,9 @@ __device__ __forceinline__ void lds_wait_barrier() {
 }
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Opaque copy: the value is the same, but the compiler cannot treat it as loop-invariant.
+__device__ __forceinline__ void launder_lane(int& x) { asm volatile("" : "+v"(x)); }
+
 // s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding)
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | 0x70 | 0xF00 | ((((n) >> 4) & 3) << 14))
 
@@ -114,7 +117,7 @@ __device__ __host__ constexpr int v_swizzle(int row) {
 // each kernel instantiates its own copies of the item loops.
 template <int D, int MODE, int KIND>
 __device__ __forceinline__ void attn_item(
-    const WorkItem& it, LdsTiles<D>& lds, uint32_t* list_vis, const uint16_t* __restrict__ q,
+    const WorkItem& it, const int tid, LdsTiles<D>& lds, uint32_t* list_vis, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
     float* __restrict__ lse, const SeqGeom& geo, int Hq, int Hkv, int G, int BT, float scale_log2,
     const Pattern& pat) {
@@ -140,13 +143,13 @@ __device__ __forceinline__ void attn_item(
   const auto tiles = [&] {
     if constexpr (MODE == MODE_LIST)
       return list_tiles(list_vis, pat, it.seq, g, Hkv, sp.qp + t0, sp.qp + t1, geo.k_pos, k_end, BK,
-                        (int)threadIdx.x, NT);
+                        tid, NT);
     else
       return KeyTilesT<MODE>(MODE, pat, sp.qp + t0, sp.qp + t1, BK, geo.k_pos, k_end);
   }();
   const int blk_shift = 31 - __clz(pat.block);  // block sizes are powers of two
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
   const int64_t kv_row = (int64_t)Hkv * D;  // elements between consecutive tokens of k / v
   const uint16_t* kbase = k + sp.k0 * kv_row + (int64_t)g * D;
@@ -497,29 +500,84 @@ __device__ __forceinline__ void attn_item(
     lse[(int64_t)qhead * geo.total_q + seq0 + qi] = (m_sc + __log2f(lt)) * LN2;
 }
 
+// Kernel arguments, in one struct (the only kernel argument) so that the item loop can
+// re-read them from the kernel argument segment for every item (see the loop below).
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  SeqGeom geo;
+  int Hq, Hkv, G, BT;
+  float scale_log2;
+  const int32_t* head_mask;
+  Pattern pat;
+  const WorkItem* items;
+  int32_t* sched;
+};
+typedef __attribute__((address_space(4))) const AttnArgs ConstArgs;
+__device__ __forceinline__ void launder(ConstArgs*& p) { asm volatile("" : "+s"(p)); }
+
+// All of a workgroup's LDS in one object.  With several LDS variables the compiler tags LDS
+// accesses with per-variable alias scopes and then makes every LDS read wait for all K/V
+// copies still in flight, which serialises the tile pipeline.
+template <int D, bool LISTS>
+struct __attribute__((aligned(1024))) KernelLds {
+  LdsTiles<D> tiles;
+  uint32_t list_vis[LISTS ? LIST_MAX_KB : 1];  // block lists: visibility per key block
+  int claim;                                    // the item claimed for the workgroup
+};
+
 // One kernel per sparse pattern kind: every launch holds full items and items of one sparse
 // kind, so each instantiation carries two item loops only (less code and fewer live scalar
-// registers than one kernel for every mode).
+// registers than one kernel for every mode).  The grid is persistent (one workgroup per
+// CU): each workgroup claims items from its XCD's queue, then from the others, until none
+// is left.
 template <int D, int KIND>
-__global__ __launch_bounds__(BF16_NW * 64, 1) void attn_bf16_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, float* __restrict__ lse, SeqGeom geo, int Hq, int Hkv, int G, int BT,
-    float scale_log2, const int32_t* __restrict__ head_mask, Pattern pat,
-    const WorkItem* __restrict__ items, const int32_t* __restrict__ n_items) {
-  constexpr bool LISTS = KIND == ELASTIC_SPARSE_BLOCK_LIST;
-  __shared__ __attribute__((aligned(1024))) LdsTiles<D> lds;
-  __shared__ uint32_t list_vis[LISTS ? LIST_MAX_KB : 1];  // block lists: visibility per key block
-  if ((int)blockIdx.x >= *n_items) return;
-  const WorkItem it = items[blockIdx.x];
-  const bool full = head_mask == nullptr || head_mask[it.seq * Hkv + it.group] != 0;
-  if (full)
-    attn_item<D, MODE_FULL, KIND>(it, lds, list_vis, q, k, v, o, lse, geo, Hq, Hkv, G, BT, scale_log2, pat);
-  else if constexpr (KIND == ELASTIC_SPARSE_STREAMING)
-    attn_item<D, MODE_STREAM, KIND>(it, lds, list_vis, q, k, v, o, lse, geo, Hq, Hkv, G, BT, scale_log2, pat);
-  else if constexpr (KIND == ELASTIC_SPARSE_BLOCK)
-    attn_item<D, MODE_BLOCK, KIND>(it, lds, list_vis, q, k, v, o, lse, geo, Hq, Hkv, G, BT, scale_log2, pat);
-  else
-    attn_item<D, MODE_LIST, KIND>(it, lds, list_vis, q, k, v, o, lse, geo, Hq, Hkv, G, BT, scale_log2, pat);
+__global__ __launch_bounds__(BF16_NW * 64, 1) void attn_bf16_kernel(AttnArgs args) {
+  __shared__ KernelLds<D, KIND == ELASTIC_SPARSE_BLOCK_LIST> shm;
+  // The arguments are read afresh for each item through an opaque pointer to the kernel
+  // argument segment, where the only explicit argument sits at offset 0: values derived from
+  // them are then computed inside the item instead of being held in registers across the
+  // whole loop (which spills).  (Taking the address of `args` would copy it to scratch.)
+  ConstArgs* const base = (ConstArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  if (base->sched != args.sched || base->items != args.items) return;  // layout as assumed
+  for (;;) {
+    ConstArgs* a = base;
+    launder(a);
+    if (threadIdx.x == 0) shm.claim = claim_item(a->sched);
+    lds_wait_barrier();
+    // uniform, and in a scalar register
+    const int idx = __builtin_amdgcn_readfirstlane(shm.claim);
+    if (idx < 0) return;  // every queue is empty
+    const WorkItem it = a->items[idx];
+    int tid = threadIdx.x;
+    launder_lane(tid);
+    const bool full = a->head_mask == nullptr || a->head_mask[it.seq * a->Hkv + it.group] != 0;
+    SeqGeom geo;
+    geo.cu_q = a->geo.cu_q, geo.cu_k = a->geo.cu_k, geo.total_q = a->geo.total_q;
+    geo.total_k = a->geo.total_k, geo.q_pos = a->geo.q_pos, geo.k_pos = a->geo.k_pos;
+    Pattern pat;
+    pat.kind = a->pat.kind, pat.sink = a->pat.sink, pat.window = a->pat.window;
+    pat.block = a->pat.block, pat.sink_blocks = a->pat.sink_blocks;
+    pat.local_blocks = a->pat.local_blocks, pat.stride_blocks = a->pat.stride_blocks;
+    pat.qblocks = a->pat.qblocks, pat.row_ptr = a->pat.row_ptr, pat.col_idx = a->pat.col_idx;
+#define ELASTIC_ITEM_ARGS it, tid, shm.tiles, shm.list_vis, a->q, a->k, a->v, a->o, a->lse, geo, \
+                          a->Hq, a->Hkv, a->G, a->BT, a->scale_log2, pat
+    if (full)
+      attn_item<D, MODE_FULL, KIND>(ELASTIC_ITEM_ARGS);
+    else if constexpr (KIND == ELASTIC_SPARSE_STREAMING)
+      attn_item<D, MODE_STREAM, KIND>(ELASTIC_ITEM_ARGS);
+    else if constexpr (KIND == ELASTIC_SPARSE_BLOCK)
+      attn_item<D, MODE_BLOCK, KIND>(ELASTIC_ITEM_ARGS);
+    else
+      attn_item<D, MODE_LIST, KIND>(ELASTIC_ITEM_ARGS);
+#undef ELASTIC_ITEM_ARGS
+    // every wave is done with the LDS tiles (O staging) and with the claim slot before the
+    // next claim
+    lds_wait_barrier();
+  }
 }
 
 }  // namespace
@@ -527,15 +585,20 @@ __global__ __launch_bounds__(BF16_NW * 64, 1) void attn_bf16_kernel(
 hipError_t launch_attn_bf16(int head_dim, const void* q, const void* k, const void* v, void* o,
                             float* lse, const SeqGeom& geo, int n_q_heads, int n_kv_heads, int BT,
                             float scale, const int32_t* head_mask, const Pattern& pat,
-                            const WorkItem* items, const int32_t* n_items, int64_t grid,
+                            const WorkItem* items, int32_t* sched, int64_t max_items,
                             hipStream_t stream) {
   const float scale_log2 = scale * 1.4426950408889634f;
   const int G = n_q_heads / n_kv_heads;
-  if (grid <= 0) return hipSuccess;
+  if (max_items <= 0) return hipSuccess;
+  hipError_t err = hipSuccess;
   auto launch = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(BF16_NW * 64), 0, stream,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
-                       geo, n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask, pat, items, n_items);
+    int64_t grid = 0;
+    err = resident_grid(reinterpret_cast<const void*>(kernel), BF16_NW * 64, &grid);
+    if (err != hipSuccess) return;
+    grid = grid < max_items ? grid : max_items;
+    const AttnArgs args{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
+                        geo, n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask, pat, items, sched};
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(BF16_NW * 64), 0, stream, args);
   };
   // without a head mask every item is full: any instantiation serves
   const int kind = head_mask == nullptr ? ELASTIC_SPARSE_STREAMING : pat.kind;
@@ -548,6 +611,7 @@ hipError_t launch_attn_bf16(int head_dim, const void* q, const void* k, const vo
     else if (kind == ELASTIC_SPARSE_BLOCK) launch(attn_bf16_kernel<64, ELASTIC_SPARSE_BLOCK>);
     else launch(attn_bf16_kernel<64, ELASTIC_SPARSE_BLOCK_LIST>);
   }
+  if (err != hipSuccess) return err;
   return hipGetLastError();
 }
 

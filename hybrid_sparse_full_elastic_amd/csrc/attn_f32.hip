@@ -21,15 +21,20 @@ __global__ __launch_bounds__(F32_ROWS, 1) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, float* __restrict__ lse, SeqGeom geo, int Hq, int Hkv, int G, int BT,
     float scale_log2, const int32_t* __restrict__ head_mask, Pattern pat,
-    const WorkItem* __restrict__ items, const int32_t* __restrict__ n_items) {
+    const WorkItem* __restrict__ items, int32_t* sched) {
   constexpr int BK = F32_BK, NT = F32_ROWS;
   constexpr int CH = BK * D / 4;  // float4 chunks per tile
   __shared__ __attribute__((aligned(16))) float k_lds[BK * D];
   __shared__ __attribute__((aligned(16))) float v_lds[BK * D];
   __shared__ uint32_t list_vis[LIST_MAX_KB];  // block lists: visibility of each key block
 
-  if ((int)blockIdx.x >= *n_items) return;
-  const WorkItem it = items[blockIdx.x];
+  // one item per workgroup, claimed from the XCD's queue (or another); the grid has at least
+  // as many workgroups as items, so every item is claimed
+  __shared__ int s_claim;
+  if (threadIdx.x == 0) s_claim = claim_item(sched);
+  __syncthreads();
+  if (s_claim < 0) return;
+  const WorkItem it = items[s_claim];
   // queries at absolute positions sp.qp + t, keys at k_pos + j
   const SeqSpan sp = seq_span(geo, it.seq);
   const int64_t seq0 = sp.q0;
@@ -143,7 +148,7 @@ __global__ __launch_bounds__(F32_ROWS, 1) void attn_f32_kernel(
 hipError_t launch_attn_f32(int head_dim, const void* q, const void* k, const void* v, void* o,
                            float* lse, const SeqGeom& geo, int n_q_heads, int n_kv_heads, int BT,
                            float scale, const int32_t* head_mask, const Pattern& pat,
-                           const WorkItem* items, const int32_t* n_items, int64_t grid,
+                           const WorkItem* items, int32_t* sched, int64_t grid,
                            hipStream_t stream) {
   const float scale_log2 = scale * 1.4426950408889634f;
   const int G = n_q_heads / n_kv_heads;
@@ -151,11 +156,11 @@ hipError_t launch_attn_f32(int head_dim, const void* q, const void* k, const voi
   if (head_dim == 128) {
     hipLaunchKernelGGL(attn_f32_kernel<128>, dim3((unsigned)grid), dim3(F32_ROWS), 0, stream,
                        (const float*)q, (const float*)k, (const float*)v, (float*)o, lse, geo,
-                       n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask, pat, items, n_items);
+                       n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask, pat, items, sched);
   } else {
     hipLaunchKernelGGL(attn_f32_kernel<64>, dim3((unsigned)grid), dim3(F32_ROWS), 0, stream,
                        (const float*)q, (const float*)k, (const float*)v, (float*)o, lse, geo,
-                       n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask, pat, items, n_items);
+                       n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask, pat, items, sched);
   }
   return hipGetLastError();
 }

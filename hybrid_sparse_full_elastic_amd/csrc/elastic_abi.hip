@@ -4,9 +4,43 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "elastic_internal.hpp"
 
 using namespace elastic;
+
+// ---------------------------------------------------------------- persistent grids
+hipError_t elastic::resident_grid(const void* kernel, int threads, int64_t* grid) {
+  struct Entry {
+    int dev;
+    const void* kernel;
+    int64_t grid;
+  };
+  static std::mutex mu;
+  static Entry cache[64];
+  static int cached = 0;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < cached; ++i)
+      if (cache[i].dev == dev && cache[i].kernel == kernel) {
+        *grid = cache[i].grid;
+        return hipSuccess;
+      }
+  }
+  int cus = 0, per_cu = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
+  if (e != hipSuccess) return e;
+  *grid = (int64_t)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached < 64) cache[cached++] = Entry{dev, kernel, *grid};
+  return hipSuccess;
+}
 
 namespace {
 
@@ -32,15 +66,16 @@ int64_t attn_max_items(int32_t dtype, int32_t batch, int64_t total_tokens, int32
 }
 
 struct AttnWorkspace {
-  size_t n_items, items, tile_prefix, total;
+  size_t sched, items, tile_prefix, cost_tmp, total;
 };
 
 AttnWorkspace attn_layout(int64_t max_items, int32_t batch) {
   AttnWorkspace w;
-  w.n_items = 0;
-  w.items = ALIGN;
+  w.sched = 0;
+  w.items = align_up(SCHED_INTS * sizeof(int32_t));
   w.tile_prefix = align_up(w.items + (size_t)max_items * sizeof(WorkItem));
-  w.total = align_up(w.tile_prefix + (size_t)(batch + 1) * sizeof(int32_t));
+  w.cost_tmp = align_up(w.tile_prefix + (size_t)(batch + 1) * sizeof(int32_t));
+  w.total = align_up(w.cost_tmp + (size_t)max_items * sizeof(int32_t));
   return w;
 }
 
@@ -249,24 +284,25 @@ int attn_call(const char* who, const void* q, const void* k, const void* v, void
   const Pattern pat = to_pattern(sparse);
   const SeqGeom geo{cu_q, cu_k, total_q, total_k, q_pos, k_pos};
   char* ws = static_cast<char*>(workspace);
-  int32_t* n_items = reinterpret_cast<int32_t*>(ws + lay.n_items);
+  int32_t* sched = reinterpret_cast<int32_t*>(ws + lay.sched);
   WorkItem* items = reinterpret_cast<WorkItem*>(ws + lay.items);
   int32_t* tile_prefix = reinterpret_cast<int32_t*>(ws + lay.tile_prefix);
+  int32_t* cost_tmp = reinterpret_cast<int32_t*>(ws + lay.cost_tmp);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   char where[96];
 
   hipError_t e = launch_plan(geo, batch, n_kv_heads, head_mask, pat, BT, BK, max_items,
-                             tile_prefix, items, n_items, st);
+                             tile_prefix, cost_tmp, items, sched, st);
   if (e != hipSuccess) {
     snprintf(where, sizeof(where), "%s: plan", who);
     return hip_fail(e, where);
   }
   if (dtype == ELASTIC_BF16)
     e = launch_attn_bf16(head_dim, q, k, v, o, lse_out, geo, n_q_heads, n_kv_heads, BT, scale,
-                         head_mask, pat, items, n_items, max_items, st);
+                         head_mask, pat, items, sched, max_items, st);
   else
     e = launch_attn_f32(head_dim, q, k, v, o, lse_out, geo, n_q_heads, n_kv_heads, BT, scale,
-                        head_mask, pat, items, n_items, max_items, st);
+                        head_mask, pat, items, sched, max_items, st);
   if (e != hipSuccess) {
     snprintf(where, sizeof(where), "%s: attention", who);
     return hip_fail(e, where);

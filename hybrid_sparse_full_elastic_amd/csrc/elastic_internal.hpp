@@ -311,21 +311,58 @@ constexpr int F32_BK = 32;
 // Query tokens per work item: the workgroup's rows hold whole tokens' G heads.
 inline int tokens_per_item(int rows, int G) { return rows / G; }
 
+// ------------------------------------------------------------------ per-XCD work queues
+// The scheduler splits the work list into one queue per XCD.  Each queue holds the items of
+// a few (sequence, KV head) groups -- a cut of the groups laid end to end, balanced by cost --
+// heaviest first, so the workgroups of one XCD stream the same K/V through their shared L2.
+// Workgroup b runs on XCD b % SCHED_NX (the dispatcher deals workgroups out round-robin); it
+// claims items from its own queue and, once that is empty, from the others (the largest
+// remaining item first), so XCDs that run ahead take over work.  Correctness does not depend
+// on the XCD mapping: every item is claimed exactly once by a counter increment.
+//
+// Header (int32, in the workspace): [0] item count, [1 + x] first item of queue x
+// (x = 0..SCHED_NX, the last entry is the count), and the claim counter of queue x at
+// [SCHED_CTR * (1 + x)], each on a 128-byte line of its own.
+constexpr int SCHED_NX = 8;
+constexpr int SCHED_CTR = 32;
+constexpr int SCHED_INTS = SCHED_CTR * (SCHED_NX + 1);
+
+// Index of the next item for the calling workgroup, or -1 when every queue is empty.  One
+// thread calls it; the result is broadcast to the workgroup.
+__device__ inline int claim_item(int32_t* sched) {
+  const int x = (int)(blockIdx.x % SCHED_NX);
+  for (int i = 0; i < SCHED_NX; ++i) {
+    const int y = (x + i) % SCHED_NX;
+    const int q0 = sched[1 + y], len = sched[2 + y] - q0;
+    int* ctr = sched + SCHED_CTR * (1 + y);
+    if (len <= 0) continue;
+    // other queues: skip them without an increment when already empty
+    if (i > 0 && __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= len) continue;
+    const int k = atomicAdd(ctr, 1);
+    if (k < len) return q0 + k;
+  }
+  return -1;
+}
+
+// Workgroups of `kernel` (block `threads`, static LDS only) that fit on the current device at
+// once: compute units x resident workgroups per unit (cached per device and kernel).
+hipError_t resident_grid(const void* kernel, int threads, int64_t* grid);
+
 // ------------------------------------------------------------------ launchers (device code)
 hipError_t launch_plan(const SeqGeom& geo, int batch, int n_kv_heads, const int32_t* head_mask,
                        const Pattern& pat, int BT, int BK, int64_t max_items, int32_t* tile_prefix,
-                       WorkItem* items, int32_t* n_items, hipStream_t stream);
+                       int32_t* cost_tmp, WorkItem* items, int32_t* sched, hipStream_t stream);
 
 hipError_t launch_attn_bf16(int head_dim, const void* q, const void* k, const void* v, void* o,
                             float* lse, const SeqGeom& geo, int n_q_heads, int n_kv_heads, int BT,
                             float scale, const int32_t* head_mask, const Pattern& pat,
-                            const WorkItem* items, const int32_t* n_items, int64_t grid,
+                            const WorkItem* items, int32_t* sched, int64_t max_items,
                             hipStream_t stream);
 
 hipError_t launch_attn_f32(int head_dim, const void* q, const void* k, const void* v, void* o,
                            float* lse, const SeqGeom& geo, int n_q_heads, int n_kv_heads, int BT,
                            float scale, const int32_t* head_mask, const Pattern& pat,
-                           const WorkItem* items, const int32_t* n_items, int64_t grid,
+                           const WorkItem* items, int32_t* sched, int64_t max_items,
                            hipStream_t stream);
 
 hipError_t launch_lse_merge(int dtype, const void* o_a, const float* lse_a, const void* o_b,

@@ -10,31 +10,54 @@
 // paperlayer summary, section 3 "Efficient Deployment" and appendix D.1 "Sparse
 // Inference").  Here the mask never leaves the device: one workgroup reads it, costs every
 // item by the number of key tiles it visits (O(n) for full items, O(sink + window) for
-// streaming ones), and counting-sorts the items by decreasing cost (longest processing time
-// first), so the hardware dispatcher hands the long causal items out first and the short
-// sparse items fill the tail.
+// streaming ones), cuts the groups (sequence, KV head) into one cost-balanced queue per XCD,
+// and counting-sorts each queue by decreasing cost (longest processing time first): the
+// workgroups of an XCD take the long causal items of their groups first, the short sparse
+// items fill the tail, and XCDs that run ahead take items from the other queues.
 #include "elastic_internal.hpp"
 
 namespace elastic {
 namespace {
 
 constexpr int PLAN_THREADS = 1024;
-constexpr int PLAN_BUCKETS = 4096;   // costs >= PLAN_BUCKETS - 1 share the last bucket
+constexpr int PLAN_BUCKETS = 1024;   // cost buckets per queue (see bucket_of)
 constexpr int PLAN_LDS_SEQ = 2048;   // sequences whose lengths / tile offsets are cached in LDS
 constexpr int PLAN_LDS_MASK = 16384; // head-mask entries cached in LDS
+constexpr int ITEM_OVERHEAD = 2;     // per-item cost (prologue, epilogue) in key tiles, for the cut
+
+// Cost bucket: exact below 768 key tiles, then 16 tiles wide; 1023 holds everything above.
+__device__ inline int bucket_of(int cost) {
+  return cost < 768 ? cost : min(768 + ((cost - 768) >> 4), PLAN_BUCKETS - 1);
+}
+
+// Block-wide inclusive scan of one value per thread (64-bit); returns the thread's inclusive
+// prefix and leaves the block total in *total.  Every thread must call it.
+__device__ inline long long block_scan(long long x, long long* tmp, long long* total) {
+  const int tid = threadIdx.x;
+  tmp[tid] = x;
+  __syncthreads();
+  for (int off = 1; off < PLAN_THREADS; off <<= 1) {
+    const long long add = tid >= off ? tmp[tid - off] : 0;
+    __syncthreads();
+    tmp[tid] += add;
+    __syncthreads();
+  }
+  const long long r = tmp[tid];
+  *total = tmp[PLAN_THREADS - 1];
+  __syncthreads();
+  return r;
+}
 
 __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     SeqGeom geo, int batch, int n_kv_heads, const int32_t* __restrict__ head_mask, Pattern pat,
     int BT, int BK, int64_t max_items, int32_t* __restrict__ tile_prefix,
-    WorkItem* __restrict__ items, int32_t* __restrict__ n_items) {
-  __shared__ int hist[PLAN_BUCKETS];
-  __shared__ int cursor[PLAN_BUCKETS];
-  __shared__ int scan_tmp[PLAN_THREADS];
+    int32_t* __restrict__ cost_tmp, WorkItem* __restrict__ items, int32_t* __restrict__ sched) {
+  __shared__ int hist[SCHED_NX * PLAN_BUCKETS];
+  __shared__ long long scan_tmp[PLAN_THREADS];
   __shared__ int s_prefix[PLAN_LDS_SEQ + 1];
   __shared__ int s_len[PLAN_LDS_SEQ];   // query rows
   __shared__ int s_klen[PLAN_LDS_SEQ];  // key rows
   __shared__ unsigned char s_full[PLAN_LDS_MASK];
-  __shared__ int carry;
   const int tid = threadIdx.x;
   const bool seq_cached = batch <= PLAN_LDS_SEQ;
   const bool mask_cached = (int64_t)batch * n_kv_heads <= PLAN_LDS_MASK;
@@ -47,30 +70,19 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
   };
 
   // 1. tile_prefix[b] = query tiles of the sequences before b (block-wide scan in chunks).
-  if (tid == 0) carry = 0;
-  for (int i = tid; i < PLAN_BUCKETS; i += PLAN_THREADS) {
-    hist[i] = 0;
-    cursor[i] = 0;
-  }
+  for (int i = tid; i < SCHED_NX * PLAN_BUCKETS; i += PLAN_THREADS) hist[i] = 0;
   if (mask_cached) {
     for (int i = tid; i < batch * n_kv_heads; i += PLAN_THREADS)
       s_full[i] = head_mask == nullptr || head_mask[i] != 0;
   }
-  __syncthreads();
+  long long carry = 0, total;
   for (int base = 0; base < batch; base += PLAN_THREADS) {
     const int b = base + tid;
     const int len = b < batch ? seq_len(b) : 0;
     const int nt = (len + BT - 1) / BT;
-    scan_tmp[tid] = nt;
-    __syncthreads();
-    for (int off = 1; off < PLAN_THREADS; off <<= 1) {
-      const int add = tid >= off ? scan_tmp[tid - off] : 0;
-      __syncthreads();
-      scan_tmp[tid] += add;
-      __syncthreads();
-    }
+    const long long inc = block_scan(nt, scan_tmp, &total);
     if (b < batch) {
-      const int pre = carry + scan_tmp[tid] - nt;
+      const int pre = (int)(carry + inc - nt);
       tile_prefix[b] = pre;
       if (seq_cached) {
         s_prefix[b] = pre;
@@ -78,11 +90,9 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
         s_klen[b] = key_len(b);
       }
     }
-    __syncthreads();
-    if (tid == PLAN_THREADS - 1) carry += scan_tmp[tid];
-    __syncthreads();
+    carry += total;
   }
-  const int total_tiles = carry;
+  const int total_tiles = (int)carry;
   if (tid == 0) {
     tile_prefix[batch] = total_tiles;
     if (seq_cached) s_prefix[batch] = total_tiles;
@@ -92,28 +102,33 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
   if (count > max_items) count = max_items;  // cannot happen for consistent cu_seqlens
   const int nitem = (int)count;
 
-  // 2. Items u = tile * n_kv_heads + g: locate, cost and histogram them.
-  auto describe = [&](int u, WorkItem& it) {
-    const int tile = u / n_kv_heads;
-    const int g = u - tile * n_kv_heads;
-    int lo = 0, hi = batch - 1;  // last b with prefix[b] <= tile
+  // Item u = tile * n_kv_heads + g, tile = tile_prefix[b] + qtile.
+  auto seq_of_tile = [&](int tile) {  // last b with prefix[b] <= tile
+    int lo = 0, hi = batch - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       const int pm = seq_cached ? s_prefix[mid] : tile_prefix[mid];
       if (pm <= tile) lo = mid; else hi = mid - 1;
     }
-    const int b = lo;
-    const int qt = tile - (seq_cached ? s_prefix[b] : tile_prefix[b]);
+    return lo;
+  };
+  auto prefix_of = [&](int b) { return seq_cached ? s_prefix[b] : tile_prefix[b]; };
+  auto locate = [&](int u, WorkItem& it) {
+    const int tile = u / n_kv_heads;
+    it.group = u - tile * n_kv_heads;
+    it.seq = seq_of_tile(tile);
+    it.qtile = tile - prefix_of(it.seq);
+  };
+  // cost: key tiles of the sequence's key range that the item's queries may see
+  auto cost_of = [&](const WorkItem& it) -> int {
+    const int b = it.seq, g = it.group;
     const int n = seq_cached ? s_len[b] : seq_len(b);
     const int nk = seq_cached ? s_klen[b] : key_len(b);
     const int qp = geo.q_pos >= 0 ? geo.q_pos : geo.k_pos + nk - n;  // absolute position of row 0
-    const int t0 = qt * BT;
+    const int t0 = it.qtile * BT;
     const int t1 = min(t0 + BT, n) - 1;
     const int mi = b * n_kv_heads + g;
     const bool full = mask_cached ? s_full[mi] != 0 : (head_mask == nullptr || head_mask[mi] != 0);
-    it.seq = b;
-    it.group = g;
-    it.qtile = qt;
     if (!full && pat.kind == ELASTIC_SPARSE_BLOCK_LIST) {
       // block lists: listed blocks of the item's query blocks (an upper bound of the union)
       const int a0 = qp + t0, a1 = qp + t1;
@@ -123,64 +138,98 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
           const int64_t r = ((int64_t)b * n_kv_heads + g) * pat.qblocks + qb;
           c += pat.row_ptr[r + 1] - pat.row_ptr[r];
         }
-      it.cost = c * (pat.block / BK);
-    } else {
-      const KeyTiles kt(full ? MODE_FULL : pat.kind, pat, qp + t0, qp + t1, BK, geo.k_pos, geo.k_pos + nk);
-      it.cost = kt.count();
+      return c * (pat.block / BK);
     }
+    const KeyTiles kt(full ? MODE_FULL : pat.kind, pat, qp + t0, qp + t1, BK, geo.k_pos, geo.k_pos + nk);
+    return kt.count();
   };
+
+  // 2. Costs, and their total weight for the cut.
+  long long wsum = 0;
   for (int u = tid; u < nitem; u += PLAN_THREADS) {
     WorkItem it;
-    describe(u, it);
-    atomicAdd(&hist[min(it.cost, PLAN_BUCKETS - 1)], 1);
+    locate(u, it);
+    const int c = cost_of(it);
+    cost_tmp[u] = c;
+    wsum += c + ITEM_OVERHEAD;
+  }
+  block_scan(wsum, scan_tmp, &total);
+  const long long W = total > 0 ? total : 1;
+
+  // 3. Cut: lay the groups (sequence, KV head) end to end, each group's query tiles in order,
+  //    and give item L of that line to XCD floor(8 * (weight before L + half its own) / W).
+  //    Line index L: sequence b owns [tile_prefix[b] * Hkv, tile_prefix[b + 1] * Hkv), KV head
+  //    major inside it.  The XCD goes into the top bits of cost_tmp[u].
+  carry = 0;
+  for (int base = 0; base < nitem; base += PLAN_THREADS) {
+    const int L = base + tid;
+    int u = -1, c = 0;
+    if (L < nitem) {
+      const int b = seq_of_tile(L / n_kv_heads);
+      const int p0 = prefix_of(b), nt = prefix_of(b + 1) - p0;
+      const int r = L - p0 * n_kv_heads;
+      const int g = r / nt, qt = r - g * nt;
+      u = (p0 + qt) * n_kv_heads + g;
+      c = cost_tmp[u];
+    }
+    const long long w = L < nitem ? c + ITEM_OVERHEAD : 0;
+    const long long inc = block_scan(w, scan_tmp, &total);
+    if (L < nitem) {
+      const long long mid2 = 2 * (carry + inc - w) + w;  // twice the item's midpoint
+      const int x = (int)min((long long)SCHED_NX - 1, mid2 * SCHED_NX / (2 * W));
+      cost_tmp[u] = c | (x << 28);
+      atomicAdd(&hist[x * PLAN_BUCKETS + (PLAN_BUCKETS - 1 - bucket_of(c))], 1);
+    }
+    carry += total;
   }
   __syncthreads();
 
-  // 3. Exclusive scan in decreasing-cost order: offset[c] = items with a larger bucket.
+  // 4. Exclusive scan over (queue, decreasing cost): hist[key] becomes the key's first slot.
   {
-    constexpr int PER = PLAN_BUCKETS / PLAN_THREADS;
+    constexpr int PER = SCHED_NX * PLAN_BUCKETS / PLAN_THREADS;
     int local[PER];
     int sum = 0;
 #pragma unroll
-    for (int r = 0; r < PER; ++r) {  // thread tid owns buckets counted from the top
-      local[r] = hist[PLAN_BUCKETS - 1 - (tid * PER + r)];
+    for (int r = 0; r < PER; ++r) {
+      local[r] = hist[tid * PER + r];
       sum += local[r];
     }
-    scan_tmp[tid] = sum;
-    __syncthreads();
-    for (int off = 1; off < PLAN_THREADS; off <<= 1) {
-      const int add = tid >= off ? scan_tmp[tid - off] : 0;
-      __syncthreads();
-      scan_tmp[tid] += add;
-      __syncthreads();
-    }
-    int run = scan_tmp[tid] - sum;
+    const long long inc = block_scan(sum, scan_tmp, &total);
+    int run = (int)(inc - sum);
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
-      hist[PLAN_BUCKETS - 1 - (tid * PER + r)] = run;
+      const int key = tid * PER + r;
+      if (key % PLAN_BUCKETS == 0) sched[1 + key / PLAN_BUCKETS] = run;  // queue start
+      hist[key] = run;
       run += local[r];
     }
   }
   __syncthreads();
 
-  // 4. Scatter.  Order inside a bucket is arbitrary; every item writes disjoint outputs with
+  // 5. Scatter.  Order inside a bucket is arbitrary; every item writes disjoint outputs with
   //    a fixed reduction order, so results do not depend on it.
   for (int u = tid; u < nitem; u += PLAN_THREADS) {
     WorkItem it;
-    describe(u, it);
-    const int bucket = min(it.cost, PLAN_BUCKETS - 1);
-    items[hist[bucket] + atomicAdd(&cursor[bucket], 1)] = it;
+    locate(u, it);
+    const int packed = cost_tmp[u];
+    it.cost = packed & 0x0fffffff;
+    const int x = (int)((unsigned)packed >> 28);
+    items[atomicAdd(&hist[x * PLAN_BUCKETS + (PLAN_BUCKETS - 1 - bucket_of(it.cost))], 1)] = it;
   }
-  if (tid == 0) *n_items = nitem;
+  if (tid == 0) {
+    sched[0] = nitem;
+    sched[1 + SCHED_NX] = nitem;
+  }
+  for (int x = tid; x < SCHED_NX; x += PLAN_THREADS) sched[SCHED_CTR * (1 + x)] = 0;
 }
 
 }  // namespace
 
 hipError_t launch_plan(const SeqGeom& geo, int batch, int n_kv_heads, const int32_t* head_mask,
                        const Pattern& pat, int BT, int BK, int64_t max_items, int32_t* tile_prefix,
-                       WorkItem* items, int32_t* n_items, hipStream_t stream) {
+                       int32_t* cost_tmp, WorkItem* items, int32_t* sched, hipStream_t stream) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, geo, batch, n_kv_heads,
-                     head_mask, pat, BT, BK, max_items, tile_prefix, items, n_items);
+                     head_mask, pat, BT, BK, max_items, tile_prefix, cost_tmp, items, sched);
   return hipGetLastError();
 }
 
