@@ -197,7 +197,7 @@ def recorded_traffic(workload):
     fields = dict(line.split(": ", 1) for line in open(path).read().splitlines()
                   if line and not line.startswith("#") and ": " in line)
     h = hashlib.sha256()
-    for name in ("attn_bf16.hip", "elastic_internal.hpp"):  # the kernel and its tile walkers
+    for name in ("attn_bf16.hip", "elastic_internal.hpp", "plan.hip"):  # kernel, tiles, schedule
         h.update(open(os.path.join(csrc, name), "rb").read())
     digest = h.hexdigest()[:16]
     if fields.get("attn_source_sha256_16") != digest:

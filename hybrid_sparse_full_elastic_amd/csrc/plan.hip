@@ -23,6 +23,7 @@ constexpr int PLAN_THREADS = 1024;
 constexpr int PLAN_BUCKETS = 1024;   // cost buckets per queue (see bucket_of)
 constexpr int PLAN_LDS_SEQ = 2048;   // sequences whose lengths / tile offsets are cached in LDS
 constexpr int PLAN_LDS_MASK = 16384; // head-mask entries cached in LDS
+constexpr int PLAN_LDS_COST = 16384; // items whose costs are cached in LDS (else cost_tmp)
 constexpr int ITEM_OVERHEAD = 2;     // per-item cost (prologue, epilogue) in key tiles, for the cut
 
 // Cost bucket: exact below 768 key tiles, then 16 tiles wide; 1023 holds everything above.
@@ -30,21 +31,32 @@ __device__ inline int bucket_of(int cost) {
   return cost < 768 ? cost : min(768 + ((cost - 768) >> 4), PLAN_BUCKETS - 1);
 }
 
-// Block-wide inclusive scan of one value per thread (64-bit); returns the thread's inclusive
-// prefix and leaves the block total in *total.  Every thread must call it.
+// Block-wide inclusive scan of one value per thread (64-bit): wave scans by shuffles, then a
+// scan of the wave totals.  Returns the thread's inclusive prefix and leaves the block total
+// in *total.  Every thread must call it; tmp holds PLAN_THREADS / 64 values.
+constexpr int PLAN_WAVES = PLAN_THREADS / 64;
 __device__ inline long long block_scan(long long x, long long* tmp, long long* total) {
-  const int tid = threadIdx.x;
-  tmp[tid] = x;
-  __syncthreads();
-  for (int off = 1; off < PLAN_THREADS; off <<= 1) {
-    const long long add = tid >= off ? tmp[tid - off] : 0;
-    __syncthreads();
-    tmp[tid] += add;
-    __syncthreads();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const long long y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
   }
-  const long long r = tmp[tid];
-  *total = tmp[PLAN_THREADS - 1];
+  if (lane == 63) tmp[w] = x;
   __syncthreads();
+  if (w == 0) {
+    long long t = lane < PLAN_WAVES ? tmp[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < PLAN_WAVES; off <<= 1) {
+      const long long y = __shfl_up(t, off, 64);
+      if (lane >= off) t += y;
+    }
+    if (lane < PLAN_WAVES) tmp[lane] = t;
+  }
+  __syncthreads();
+  const long long r = x + (w > 0 ? tmp[w - 1] : 0);
+  *total = tmp[PLAN_WAVES - 1];
+  __syncthreads();  // tmp is reused by the next call
   return r;
 }
 
@@ -53,11 +65,12 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     int BT, int BK, int64_t max_items, int32_t* __restrict__ tile_prefix,
     int32_t* __restrict__ cost_tmp, WorkItem* __restrict__ items, int32_t* __restrict__ sched) {
   __shared__ int hist[SCHED_NX * PLAN_BUCKETS];
-  __shared__ long long scan_tmp[PLAN_THREADS];
+  __shared__ long long scan_tmp[PLAN_WAVES];
   __shared__ int s_prefix[PLAN_LDS_SEQ + 1];
   __shared__ int s_len[PLAN_LDS_SEQ];   // query rows
   __shared__ int s_klen[PLAN_LDS_SEQ];  // key rows
   __shared__ unsigned char s_full[PLAN_LDS_MASK];
+  __shared__ int s_cost[PLAN_LDS_COST];
   const int tid = threadIdx.x;
   const bool seq_cached = batch <= PLAN_LDS_SEQ;
   const bool mask_cached = (int64_t)batch * n_kv_heads <= PLAN_LDS_MASK;
@@ -144,22 +157,28 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     return kt.count();
   };
 
+  // per-item cost (then cost | XCD << 28): in LDS when it fits, else in the workspace
+  int* const cost = nitem <= PLAN_LDS_COST ? s_cost : cost_tmp;
+
   // 2. Costs, and their total weight for the cut.
   long long wsum = 0;
   for (int u = tid; u < nitem; u += PLAN_THREADS) {
     WorkItem it;
     locate(u, it);
     const int c = cost_of(it);
-    cost_tmp[u] = c;
+    cost[u] = c;
     wsum += c + ITEM_OVERHEAD;
   }
   block_scan(wsum, scan_tmp, &total);
   const long long W = total > 0 ? total : 1;
 
-  // 3. Cut: lay the groups (sequence, KV head) end to end, each group's query tiles in order,
-  //    and give item L of that line to XCD floor(8 * (weight before L + half its own) / W).
-  //    Line index L: sequence b owns [tile_prefix[b] * Hkv, tile_prefix[b + 1] * Hkv), KV head
-  //    major inside it.  The XCD goes into the top bits of cost_tmp[u].
+  // 3. Cut: lay the groups (sequence, KV head) end to end and give item L of that line to XCD
+  //    floor(8 * (weight before L + half its own) / W).  Line index L: sequence b owns
+  //    [tile_prefix[b] * Hkv, tile_prefix[b + 1] * Hkv), KV head major inside it, and a
+  //    group's query tiles alternate from both ends (0, last, 1, last - 1, ...), so that any
+  //    stretch of the line -- a queue -- holds long and short items alike (causal costs grow
+  //    with the query tile) and every queue ends on short items.  The XCD goes into the top
+  //    bits of cost[u].
   carry = 0;
   for (int base = 0; base < nitem; base += PLAN_THREADS) {
     const int L = base + tid;
@@ -168,16 +187,17 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
       const int b = seq_of_tile(L / n_kv_heads);
       const int p0 = prefix_of(b), nt = prefix_of(b + 1) - p0;
       const int r = L - p0 * n_kv_heads;
-      const int g = r / nt, qt = r - g * nt;
+      const int g = r / nt, j = r - g * nt;
+      const int qt = (j & 1) ? nt - 1 - (j >> 1) : (j >> 1);  // 0, nt-1, 1, nt-2, ...
       u = (p0 + qt) * n_kv_heads + g;
-      c = cost_tmp[u];
+      c = cost[u];
     }
     const long long w = L < nitem ? c + ITEM_OVERHEAD : 0;
     const long long inc = block_scan(w, scan_tmp, &total);
     if (L < nitem) {
       const long long mid2 = 2 * (carry + inc - w) + w;  // twice the item's midpoint
       const int x = (int)min((long long)SCHED_NX - 1, mid2 * SCHED_NX / (2 * W));
-      cost_tmp[u] = c | (x << 28);
+      cost[u] = c | (x << 28);
       atomicAdd(&hist[x * PLAN_BUCKETS + (PLAN_BUCKETS - 1 - bucket_of(c))], 1);
     }
     carry += total;
@@ -211,7 +231,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
   for (int u = tid; u < nitem; u += PLAN_THREADS) {
     WorkItem it;
     locate(u, it);
-    const int packed = cost_tmp[u];
+    const int packed = cost[u];
     it.cost = packed & 0x0fffffff;
     const int x = (int)((unsigned)packed >> 28);
     items[atomicAdd(&hist[x * PLAN_BUCKETS + (PLAN_BUCKETS - 1 - bucket_of(it.cost))], 1)] = it;
