@@ -3,5 +3,6 @@ from .elastic_oracle import (  # noqa: F401
     allowed, as_f64, attention, attention_kv, block_list_from_pattern, block_list_resolve,
     block_streaming, chunked_prefill, decode_bf16,
     effective_flops, effective_sparsity, entries, head_modes, lse_merge, mean_exact,
-    model_sparsity_ratio, pooled_rows, route, row_key_counts,
+    model_sparsity_ratio, pooled_rows, retrieval_scores, route, row_key_counts,
+    static_assignment,
 )

@@ -53,6 +53,16 @@ What is computed (readings of points the summary leaves open are marked READING)
     block_streaming  READING: the block-granular form of sink + window streaming is the
                      block pattern with block 64, ceil(sink / 64) sink blocks, a window of
                      window / 64 blocks that includes the query's own block, and no stride.
+* Static retrieval-score head assignment (appendix C.1 "Retrieval Score Calculation"):
+    retrieval_scores   S = attention mass of a sequence's last token on the needle positions,
+                       sum over j in needle of softmax_j(scale <q_last, k_j>) over all keys
+                       of the sequence (the last token sees every key).  READING: the needle
+                       is one contiguous span [begin, end) of key positions (clipped to the
+                       sequence); a KV head's score is the mean of its G query heads' scores;
+                       an empty sequence scores 0.
+    static_assignment  k = floor((1 - omega_msr) * N) of the N (layer, KV head) units with
+                       the highest scores stay full, the rest sparse.  READING: k in fp64;
+                       equal scores rank by lower unit index; NaN ranks below every number.
 """
 from __future__ import annotations
 
@@ -460,3 +470,52 @@ def chunked_prefill(q, k, v, cu_seqlens, head_mask, sparse, chunk: int,
             lse[:, c0:c1] = lb
     return o, lse
 
+
+
+# ----------------------------------------------------------------------------- static assignment
+def retrieval_scores(q, k, cu_seqlens, needle, scale: Optional[float] = None):
+    """Appendix C.1 "Retrieval Score Calculation": for each sequence b and query head h, the
+    softmax weight that the last token of b puts on the needle span needle[b] = (begin, end)
+    (local key positions, clipped to the sequence), over all keys of b.
+
+    Returns (scores_q [B, Hq], scores_kv [B, Hkv]); a KV head's score is the mean over its
+    query heads.  Two-pass softmax in fp64: m = max_j s_j, S = sum_needle e^(s_j - m) /
+    sum_all e^(s_j - m)."""
+    Q, K = as_f64(q), as_f64(k)
+    T, Hq, D = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    sc = D ** -0.5 if scale is None else scale
+    cu = _seq_bounds(cu_seqlens, T)
+    B = len(cu) - 1
+    nd = np.asarray(needle, dtype=np.int64).reshape(B, 2)
+    sq = np.zeros((B, Hq))
+    for b in range(B):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        n = hi - lo
+        if n == 0:
+            continue
+        a, e = max(0, int(nd[b, 0])), min(n, int(nd[b, 1]))
+        for h in range(Hq):
+            s = sc * (K[lo:hi, h // G, :] @ Q[hi - 1, h, :])
+            w = np.exp(s - s.max())
+            sq[b, h] = (w[a:e].sum() if e > a else 0.0) / w.sum()
+    skv = sq.reshape(B, Hkv, G).mean(axis=2)
+    return sq, skv
+
+
+def static_assignment(scores, omega_msr: float) -> np.ndarray:
+    """Appendix C.1 "Sparsity Assignment": of the N units (all layers' KV heads, flattened in
+    order) the k = floor((1 - omega_msr) * N) with the highest scores stay full (mask 1), the
+    rest are sparse (0).  Ties rank by lower index; NaN ranks below every number."""
+    s = np.asarray(scores, dtype=np.float64).reshape(-1)
+    n = s.size
+    k = int(math.floor((1.0 - float(omega_msr)) * n))
+    k = max(0, min(n, k))
+    key = np.where(np.isnan(s), -np.inf, s)
+    nan = np.isnan(s)
+    # descending score; NaN after -inf; then ascending index
+    order = sorted(range(n), key=lambda i: (nan[i], -key[i], i))
+    mask = np.zeros(n, dtype=np.int32)
+    mask[order[:k]] = 1
+    return mask.reshape(np.shape(scores))
