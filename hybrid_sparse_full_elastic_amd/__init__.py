@@ -7,5 +7,6 @@ if the library is missing, importing this package raises.
 """
 from ._binding import (  # noqa: F401
     ABI_VERSION, ElasticError, LIB_PATH, SparseCfg, attn_entries, attn_prefill, attn_prefill_kv,
-    attn_workspace_size, block_list_entries, lib, lse_merge, route, route_workspace_size, sparse_cfg,
+    attn_workspace_size, block_list_entries, lib, lse_merge, retrieval_scores,
+    retrieval_workspace_size, route, route_workspace_size, sparse_cfg, static_assignment,
 )

@@ -10,7 +10,7 @@ import torch
 # ELASTIC_LIB selects another build of the same library (e.g. a tuning variant).
 LIB_PATH = os.environ.get("ELASTIC_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                          "libelastic.so")
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
 BF16, FP32 = 0, 1
@@ -64,6 +64,13 @@ def _load():
     L.elastic_attn_entries.restype = C.c_int
     L.elastic_attn_entries.argtypes = [C.POINTER(i32), i32, C.POINTER(i32), i32, i32,
                                        C.POINTER(SparseCfg), C.POINTER(i64)]
+    L.elastic_retrieval_workspace_size.restype = sz
+    L.elastic_retrieval_workspace_size.argtypes = [i32, i32, i32]
+    L.elastic_retrieval_scores.restype = C.c_int
+    L.elastic_retrieval_scores.argtypes = [vp, vp, i32, vp, i32, i64, i32, i32, i32, i32, f32, vp,
+                                           vp, vp, vp, sz, vp]
+    L.elastic_static_assignment.restype = C.c_int
+    L.elastic_static_assignment.argtypes = [vp, i32, C.c_double, vp, vp]
     if L.elastic_abi_version() != ABI_VERSION:
         raise ImportError(f"libelastic ABI {L.elastic_abi_version()} != binding ABI {ABI_VERSION}")
     return L
@@ -307,6 +314,63 @@ def lse_merge(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b: 
     if st != OK:
         raise ElasticError(st, "elastic_lse_merge")
     return out, lse_out
+
+
+def retrieval_workspace_size(batch: int, max_seqlen: int, n_q_heads: int) -> int:
+    return int(lib.elastic_retrieval_workspace_size(batch, max_seqlen, n_q_heads))
+
+
+def retrieval_scores(q: torch.Tensor, k: torch.Tensor, needle: torch.Tensor,
+                     cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None,
+                     softmax_scale: float = 0.0, workspace: Optional[torch.Tensor] = None,
+                     stream=None):
+    """Attention mass of each sequence's last token on its needle span: returns
+    (scores_q [B, Hq], scores_kv [B, Hkv]) fp32.  ``needle`` is int32 [B, 2] (begin, end)."""
+    for name, t in (("q", q), ("k", k)):
+        _check_dev(name, t)
+        if t.dim() != 3:
+            raise ValueError(f"{name} must be [T, heads, head_dim]")
+    if q.dtype not in (torch.bfloat16, torch.float32) or k.dtype != q.dtype:
+        raise ValueError("q and k must share dtype bf16 or fp32")
+    T, hq, D = q.shape
+    hkv = k.shape[1]
+    if k.shape != (T, hkv, D):
+        raise ValueError("k must be [T, n_kv_heads, head_dim] matching q")
+    B = _seq_args(cu_seqlens, T)
+    _check_dev("needle", needle, torch.int32)
+    if needle.shape != (B, 2):
+        raise ValueError("needle must be int32 [batch, 2]")
+    ms = int(max_seqlen if max_seqlen is not None else T)
+    sq = torch.empty((B, hq), dtype=torch.float32, device=q.device)
+    skv = torch.empty((B, hkv), dtype=torch.float32, device=q.device)
+    need = retrieval_workspace_size(B, ms, hq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dtype = BF16 if q.dtype == torch.bfloat16 else FP32
+    st = lib.elastic_retrieval_scores(_ptr(q), _ptr(k), dtype, _ptr(cu_seqlens), B, T, ms, hq, hkv,
+                                      D, float(softmax_scale), _ptr(needle), _ptr(sq), _ptr(skv),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(stream))
+    if st != OK:
+        raise ElasticError(st, "elastic_retrieval_scores")
+    return sq, skv
+
+
+def static_assignment(scores: torch.Tensor, omega_msr: float, out: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """Full (1) / sparse (0) mask of the same shape as ``scores`` (fp32, any shape, e.g.
+    [layers, n_kv_heads]): the floor((1 - omega_msr) * N) highest scores stay full."""
+    _check_dev("scores", scores, torch.float32)
+    if out is None:
+        out = torch.empty(scores.shape, dtype=torch.int32, device=scores.device)
+    _check_dev("out", out, torch.int32)
+    if out.shape != scores.shape:
+        raise ValueError("out must match scores")
+    st = lib.elastic_static_assignment(_ptr(scores), scores.numel(), float(omega_msr), _ptr(out),
+                                       _stream(stream))
+    if st != OK:
+        raise ElasticError(st, "elastic_static_assignment")
+    return out
 
 
 def attn_entries(seqlens, head_mask, n_q_heads: int, n_kv_heads: int, sparse=None) -> int:

@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <math.h>
 #include <mutex>
 
 #include "elastic_internal.hpp"
@@ -351,6 +352,54 @@ int elastic_lse_merge(const void* o_a, const float* lse_a, const void* o_b, cons
   const hipError_t e = launch_lse_merge(dtype, o_a, lse_a, o_b, lse_b, o_out, lse_out, rows,
                                         n_heads, head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "elastic_lse_merge");
+  return ELASTIC_OK;
+}
+
+size_t elastic_retrieval_workspace_size(int32_t batch, int32_t max_seqlen, int32_t n_q_heads) {
+  if (batch < 0 || n_q_heads < 1) return 0;
+  return align_up((size_t)batch * n_q_heads * (size_t)retrieval_chunks(max_seqlen) * 3 *
+                  sizeof(float)) + ALIGN;
+}
+
+int elastic_retrieval_scores(const void* q, const void* k, int32_t dtype,
+                             const int32_t* cu_seqlens, int32_t batch, int64_t total_tokens,
+                             int32_t max_seqlen, int32_t n_q_heads, int32_t n_kv_heads,
+                             int32_t head_dim, float softmax_scale, const int32_t* needle,
+                             float* scores_q, float* scores_kv, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (batch < 0 || total_tokens < 0 || max_seqlen < 0) return ELASTIC_EINVAL;
+  if (n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads != 0) return ELASTIC_EINVAL;
+  if (cu_seqlens == nullptr && batch > 1) return ELASTIC_EINVAL;
+  if (cu_seqlens == nullptr && batch == 1 && total_tokens > max_seqlen) return ELASTIC_EINVAL;
+  if (dtype != ELASTIC_BF16 && dtype != ELASTIC_FP32) return ELASTIC_EUNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return ELASTIC_EUNSUPPORTED;
+  if (batch == 0) return ELASTIC_OK;
+  if (!q || !k || !needle || (!scores_q && !scores_kv)) return ELASTIC_EINVAL;
+  if (((uintptr_t)q | (uintptr_t)k) % 16 != 0) return ELASTIC_EINVAL;
+  // grid: chunks x (KV heads x slices of 8 query heads) x sequences
+  if (batch > 65535 || (int64_t)n_kv_heads * ((n_q_heads / n_kv_heads + 7) / 8) > 65535)
+    return ELASTIC_EUNSUPPORTED;
+  const size_t need = elastic_retrieval_workspace_size(batch, max_seqlen, n_q_heads);
+  if (workspace == nullptr || workspace_bytes < need) return ELASTIC_EWORKSPACE;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
+  const hipError_t e = launch_retrieval(dtype, head_dim, q, k, cu_seqlens, total_tokens, batch,
+                                        max_seqlen, n_q_heads, n_kv_heads, scale, needle,
+                                        static_cast<float*>(workspace), scores_q, scores_kv,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "elastic_retrieval_scores");
+  return ELASTIC_OK;
+}
+
+int elastic_static_assignment(const float* scores, int32_t n_units, double omega_msr,
+                              int32_t* mask_out, void* stream) {
+  if (n_units < 0 || !(omega_msr >= 0.0 && omega_msr <= 1.0)) return ELASTIC_EINVAL;
+  if (n_units > ELASTIC_ASSIGN_MAX_UNITS) return ELASTIC_EUNSUPPORTED;
+  if (n_units == 0) return ELASTIC_OK;
+  if (!scores || !mask_out) return ELASTIC_EINVAL;
+  int k = (int)floor((1.0 - omega_msr) * (double)n_units);  // the pages' formula, in fp64
+  k = k < 0 ? 0 : (k > n_units ? n_units : k);
+  const hipError_t e = launch_assign(scores, n_units, k, mask_out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "elastic_static_assignment");
   return ELASTIC_OK;
 }
 

@@ -365,6 +365,15 @@ hipError_t launch_attn_f32(int head_dim, const void* q, const void* k, const voi
                            const WorkItem* items, int32_t* sched, int64_t max_items,
                            hipStream_t stream);
 
+// Retrieval scores: keys per partial workgroup, chunk count for a sequence length bound.
+constexpr int RET_CHUNK = 1024;
+int64_t retrieval_chunks(int32_t max_seqlen);
+hipError_t launch_retrieval(int dtype, int head_dim, const void* q, const void* k,
+                            const int32_t* cu, int64_t total, int batch, int max_seqlen, int Hq,
+                            int Hkv, float scale, const int32_t* needle, float* part,
+                            float* scores_q, float* scores_kv, hipStream_t stream);
+hipError_t launch_assign(const float* scores, int n, int k, int32_t* mask, hipStream_t stream);
+
 hipError_t launch_lse_merge(int dtype, const void* o_a, const float* lse_a, const void* o_b,
                             const float* lse_b, void* o_out, float* lse_out, int64_t rows,
                             int heads, int head_dim, hipStream_t stream);

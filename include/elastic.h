@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define ELASTIC_ABI_VERSION 2
+#define ELASTIC_ABI_VERSION 3
 
 enum elastic_status {
   ELASTIC_OK = 0,
@@ -209,6 +209,43 @@ int elastic_attn_prefill_kv(const void* q, const void* k, const void* v, void* o
 int elastic_lse_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
                       void* o_out, float* lse_out, int32_t dtype, int64_t rows, int32_t n_heads,
                       int32_t head_dim, void* stream);
+
+/*
+ * Retrieval scores of the pages' static head assignment (summary appendix C.1 "Retrieval
+ * Score Calculation"): for sequence b and query head h, the attention weight that the last
+ * token of b puts on the needle span [needle[2b], needle[2b+1]) (local key positions, clipped
+ * to the sequence), softmax over all keys of b with scale softmax_scale (<= 0: head_dim^-1/2):
+ *   scores_q[b, h]  = sum_{j in needle} exp(s_j) / sum_j exp(s_j),  s_j = scale <q_last, k_j>
+ *   scores_kv[b, g] = mean of scores_q[b, h] over the G query heads of KV head g.
+ * An empty sequence scores 0.  q [total_tokens, n_q_heads, head_dim] (only each sequence's
+ * last row is read), k [total_tokens, n_kv_heads, head_dim]; cu_seqlens as for
+ * elastic_attn_prefill; needle int32 [batch, 2] device; scores_q fp32 [batch, n_q_heads] and
+ * scores_kv fp32 [batch, n_kv_heads] device, either may be NULL (not both).  q and k 16-byte
+ * aligned.  fp32 accumulation; reads every key once (HBM-bound).
+ * Errors: ELASTIC_EINVAL (pointers, shapes, alignment), ELASTIC_EUNSUPPORTED (dtype,
+ * head_dim, more than 65535 sequences), ELASTIC_EWORKSPACE.
+ */
+size_t elastic_retrieval_workspace_size(int32_t batch, int32_t max_seqlen, int32_t n_q_heads);
+int elastic_retrieval_scores(const void* q, const void* k, int32_t dtype,
+                             const int32_t* cu_seqlens, int32_t batch, int64_t total_tokens,
+                             int32_t max_seqlen, int32_t n_q_heads, int32_t n_kv_heads,
+                             int32_t head_dim, float softmax_scale, const int32_t* needle,
+                             float* scores_q, float* scores_kv, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
+ * Static head assignment (summary appendix C.1 "Sparsity Assignment"): of the n_units
+ * scores (device fp32, e.g. [layers, n_kv_heads] flattened), the
+ *   k = floor((1 - omega_msr) * n_units)       (evaluated in double)
+ * highest stay full: mask_out[i] = 1, the rest 0 (device int32 [n_units]).  Equal scores rank
+ * by lower index; NaN ranks below every number.  A layer's slice of mask_out is a forced head
+ * mask for elastic_attn_prefill.  One workgroup, O(n_units^2) comparisons.
+ * Errors: ELASTIC_EINVAL (pointers, omega_msr outside [0, 1]), ELASTIC_EUNSUPPORTED
+ * (n_units > ELASTIC_ASSIGN_MAX_UNITS).
+ */
+#define ELASTIC_ASSIGN_MAX_UNITS 16384
+int elastic_static_assignment(const float* scores, int32_t n_units, double omega_msr,
+                              int32_t* mask_out, void* stream);
 
 /*
  * Host-only work counter (no HIP call): the number of allowed (query, key) score entries

@@ -221,3 +221,36 @@ def test_block_list_validation_without_gpu():
     # key ranges must start on a block of the list
     assert _attn_kv(sparse=ext.SparseCfg(2, 0, 0, 128, 0, 0, 0, 16, 0x1000, 0x1000), mask=FAKE,
                     kpos=64) == EINVAL
+
+
+def _ret(**kw):
+    a = dict(q=FAKE, k=FAKE, dtype=0, cu=None, batch=1, T=1024, ms=1024, hq=32, hkv=8, D=128,
+             scale=0.0, needle=FAKE, sq=FAKE, skv=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return L.elastic_retrieval_scores(a["q"], a["k"], a["dtype"], a["cu"], a["batch"], a["T"],
+                                      a["ms"], a["hq"], a["hkv"], a["D"], a["scale"], a["needle"],
+                                      a["sq"], a["skv"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_retrieval_and_assignment_validation_without_gpu():
+    EINVAL, EUNS, EWS = 1, 2, 3
+    assert _ret(needle=None) == EINVAL
+    assert _ret(sq=None, skv=None) == EINVAL
+    assert _ret(q=None) == EINVAL
+    assert _ret(hq=30) == EINVAL                      # not a multiple of n_kv_heads
+    assert _ret(batch=2) == EINVAL                    # several sequences need cu_seqlens
+    assert _ret(T=2048) == EINVAL                     # one sequence longer than max_seqlen
+    assert _ret(q=C.c_void_p(0x1008)) == EINVAL      # 16-byte alignment
+    assert _ret(D=96) == EUNS
+    assert _ret(dtype=7) == EUNS
+    assert _ret(ws=None) == EWS
+    need = ext.retrieval_workspace_size(1, 1024, 32)
+    assert need > 0 and _ret(wsb=need - 1) == EWS
+    assert _ret(batch=0, q=None, k=None, needle=None) == 0   # nothing to score
+    a = L.elastic_static_assignment
+    assert a(FAKE, 8, -0.1, FAKE, None) == EINVAL
+    assert a(FAKE, 8, 1.5, FAKE, None) == EINVAL
+    assert a(FAKE, -1, 0.5, FAKE, None) == EINVAL
+    assert a(None, 8, 0.5, FAKE, None) == EINVAL
+    assert a(FAKE, 16385, 0.5, FAKE, None) == EUNS
+    assert a(None, 0, 0.5, None, None) == 0                  # no units: no-op
