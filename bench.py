@@ -170,6 +170,8 @@ def main():
         rec["supplements"] = supplements(ext, torch, w, q, k, v, o, cu, ws_attn, stream, args)
         if w.batch == 1:
             rec["supplements"]["deployment"] = deployment(ext, torch, w, q, k, v, o, mask, ws_attn, stream)
+        if w.batch == 1:
+            rec["supplements"]["static_assignment"] = static_assignment_detail(ext, torch, w, q, k, stream)
         if has_router:
             rec["supplements"]["router"] = router_detail(ext, torch, hidden, w1, w2, cu, threshold,
                                                          logits, mask.clone(), ws_route, stream)
@@ -282,6 +284,25 @@ def deployment(ext, torch, w, q, k, v, o, mask, ws, stream):
             "block_lists_sel8_all_heads_tflops": round(4 * D * ent_sel / ms_sel / 1e9, 2),
             "block_lists_sel8_router_mask_ms": round(ms_selm, 4),
             "block_lists_sel8_router_mask_tflops": round(4 * D * ent_selm / ms_selm / 1e9, 2)}
+
+
+def static_assignment_detail(ext, torch, w, q, k, stream):
+    """The pages' static baseline (appendix C.1): retrieval scores of the layer's last token on
+    a 64-token needle (reads every key once: HBM-bound) and the ranking of 32 layers x the KV
+    heads by those scores."""
+    T, hq, D = q.shape
+    hkv = k.shape[1]
+    nd = torch.tensor([[T // 2, T // 2 + 64]], dtype=torch.int32, device=q.device)
+    ws = torch.empty(ext.retrieval_workspace_size(1, T, hq), dtype=torch.uint8, device=q.device)
+    ms = _time_attn(ext, torch, stream, lambda: ext.retrieval_scores(q, k, nd, workspace=ws))
+    nbytes = T * hkv * D * k.element_size() + hq * D * q.element_size()
+    scores = torch.rand((32, hkv), generator=torch.Generator(device=q.device).manual_seed(5),
+                        device=q.device)
+    out = torch.empty((32, hkv), dtype=torch.int32, device=q.device)
+    ms_a = _time_attn(ext, torch, stream, lambda: ext.static_assignment(scores, 0.375, out=out))
+    return {"retrieval_scores_us": round(ms * 1e3, 2),
+            "retrieval_scores_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "assignment_32x%d_us" % hkv: round(ms_a * 1e3, 2)}
 
 
 def router_detail(ext, torch, hidden, w1, w2, cu, threshold, logits, mask, ws, stream, reps=10):

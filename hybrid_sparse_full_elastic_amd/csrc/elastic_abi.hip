@@ -376,6 +376,7 @@ int elastic_retrieval_scores(const void* q, const void* k, int32_t dtype,
   if (batch == 0) return ELASTIC_OK;
   if (!q || !k || !needle || (!scores_q && !scores_kv)) return ELASTIC_EINVAL;
   if (((uintptr_t)q | (uintptr_t)k) % 16 != 0) return ELASTIC_EINVAL;
+  if (n_q_heads / n_kv_heads > RET_MAX_G) return ELASTIC_EUNSUPPORTED;
   // grid: chunks x (KV heads x slices of 8 query heads) x sequences
   if (batch > 65535 || (int64_t)n_kv_heads * ((n_q_heads / n_kv_heads + 7) / 8) > 65535)
     return ELASTIC_EUNSUPPORTED;

@@ -366,7 +366,8 @@ hipError_t launch_attn_f32(int head_dim, const void* q, const void* k, const voi
                            hipStream_t stream);
 
 // Retrieval scores: keys per partial workgroup, chunk count for a sequence length bound.
-constexpr int RET_CHUNK = 1024;
+constexpr int RET_CHUNK = 256;
+constexpr int RET_MAX_G = 1024;  // query heads per KV head the score combine supports
 int64_t retrieval_chunks(int32_t max_seqlen);
 hipError_t launch_retrieval(int dtype, int head_dim, const void* q, const void* k,
                             const int32_t* cu, int64_t total, int batch, int max_seqlen, int Hq,

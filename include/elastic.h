@@ -223,7 +223,7 @@ int elastic_lse_merge(const void* o_a, const float* lse_a, const void* o_b, cons
  * scores_kv fp32 [batch, n_kv_heads] device, either may be NULL (not both).  q and k 16-byte
  * aligned.  fp32 accumulation; reads every key once (HBM-bound).
  * Errors: ELASTIC_EINVAL (pointers, shapes, alignment), ELASTIC_EUNSUPPORTED (dtype,
- * head_dim, more than 65535 sequences), ELASTIC_EWORKSPACE.
+ * head_dim, more than 65535 sequences or 1024 query heads per KV head), ELASTIC_EWORKSPACE.
  */
 size_t elastic_retrieval_workspace_size(int32_t batch, int32_t max_seqlen, int32_t n_q_heads);
 int elastic_retrieval_scores(const void* q, const void* k, int32_t dtype,
