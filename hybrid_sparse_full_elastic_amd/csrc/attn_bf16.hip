@@ -12,15 +12,18 @@
 //    group), 8 waves of 32 query rows.  Every wave fits in 256 VGPRs, so two waves share a
 //    SIMD.
 //  * S^T = K . Q^T with v_mfma_f32_32x32x16_bf16: every lane holds one query column, so the
-//    softmax row statistics are per-lane; one v_permlane32_swap per tile finishes the row
-//    maximum.  Q stays in registers for the whole item.
+//    softmax row statistics are per-lane (a v_permlane32_swap joins the two halves of a
+//    column).  Q stays in registers for the whole item.
 //  * O^T = V^T . P^T: P^T comes straight from the S^T accumulators (bf16) with a fixed
 //    key-slot permutation, and ds_read_b64_tr_b16 builds the matching V^T operand from the
 //    row-major V tile.  The rescale of O by the running maximum is a per-lane multiply.
 //  * Online softmax in the exp2 domain with the softmax scale and log2(e) folded into one
 //    FMA; fp32 accumulation throughout; the row sum adds the bf16 weights the P.V product
-//    uses (v_dot2) so numerator and denominator agree.  The running maximum is raised lazily
-//    (only when a tile exceeds it by 2^8), so O is almost never rescaled.
+//    uses (v_dot2) so numerator and denominator agree.  The running maximum m comes from the
+//    first tile and is raised only when a tile's weights 2^(s - m) grow past 2^64, which the
+//    row sums reveal for free (a partial sum above 2^70): such a tile is redone with its own
+//    maximum and O rescaled.  No per-tile maximum is computed; fp32 holds the weights and
+//    sums with room to spare, and the result is exact in exact arithmetic for any m.
 //  * Masks are evaluated only on tiles that cross a causal, sink, window or block boundary,
 //    and tiles no query of the item may see are never loaded (streaming items cost
 //    O(sink + window), not O(n)).  Each item runs a loop compiled for its mode.
@@ -32,7 +35,7 @@
 //  * Per tile step j, two instruction regions fenced with sched_barrier so the issue order is
 //    the written one: the Q.K^T MFMAs of tile j+1 with the exp2 / bf16 packing / row sums of
 //    tile j between them (K fragments read three MFMAs ahead), then the P.V MFMAs of tile j
-//    with the transposing V reads (two ahead) and the maximum of tile j+1 between them.  A
+//    with the transposing V reads (two ahead) between them.  A
 //    wave keeps its MFMA pipe fed while its own softmax work issues beside it, and the two
 //    waves sharing a SIMD fill each other's gaps.  The mask of an edge tile sits between the
 //    regions; one barrier per step.
@@ -128,7 +131,6 @@ __device__ __forceinline__ void attn_item(
   constexpr int CPT = BK * CPR / NT;  // DMA chunks per thread per tile and operand
   static_assert(CPT >= 1 && CPT * NT == BK * CPR, "tile split");
   static_assert(NW * 32 * D * 2 <= sizeof(LdsTiles<D>), "O staging fits in the tile slots");
-  constexpr float SLACK = 8.0f;       // lazy rescale threshold (log2 units)
   constexpr int SLOT = BK * D;        // elements per LDS slot
 
   // rows of this sequence: queries at absolute positions sp.qp + t, keys at k_pos + j
@@ -274,10 +276,10 @@ __device__ __forceinline__ void attn_item(
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
   float m_sc = -1.0e30f;  // finite: fully masked tiles give p = 0 and never raise it
-  float l_run = 0.f, alpha = 1.f;
-  bool pending = false;   // wave-uniform: O and l wait for a multiply by alpha
+  float l_run = 0.f;
 
-  auto update_max = [&](f32x16 (&s)[2]) {
+  // m from the first tile (O and l are still zero, so nothing is rescaled)
+  auto first_max = [&](f32x16 (&s)[2]) {
     float m0 = max3f(s[0][0], s[1][0], s[0][1]);
     float m1 = max3f(s[1][1], s[0][2], s[1][2]);
 #pragma unroll
@@ -285,13 +287,7 @@ __device__ __forceinline__ void attn_item(
       m0 = max3f(m0, s[0][e], s[1][e]);
       m1 = max3f(m1, s[0][e + 1], s[1][e + 1]);
     }
-    const float ms = half_max(max3f(m0, m1, max3f(s[0][15], s[1][15], m0))) * c;
-    if (__builtin_amdgcn_ballot_w64(ms > m_sc + SLACK) != 0) {
-      const float mn = fmaxf(m_sc, ms);
-      alpha = __builtin_amdgcn_exp2f(m_sc - mn);
-      m_sc = mn;
-      pending = true;
-    }
+    m_sc = fmaxf(m_sc, half_max(max3f(m0, m1, max3f(s[0][15], s[1][15], m0))) * c);
   };
 
   // ---- tile schedule: kt_cur = tile j, kt_n1/2/3 = tiles j+1..j+3 (-1 when absent)
@@ -319,8 +315,7 @@ __device__ __forceinline__ void attn_item(
     qk(kslot, s0);
     __syncthreads();  // every wave is done with K slot 0 before step 0 refills it
     if (tiles.needs_mask(kt_cur)) apply_mask(s0, kt_cur);
-    update_max(s0);
-    pending = false;  // O and l are still zero
+    first_max(s0);
     int sj = 0;       // LDS slot of tile j (tile t lives in slot t mod 3)
 
     // One step on tile j: DMA K_{j+3} and V_{j+2}; S_{j+1} = K_{j+1} Q^T; p_j = exp2(c s_j - m);
@@ -341,14 +336,6 @@ __device__ __forceinline__ void attn_item(
       } else {
         if (kt_n3 >= 0) dma(kbase, kt_n3, kslot + sj * SLOT, k_voff);   // slot of K_j, read last step
         if (kt_n2 >= 0) dma(vbase, kt_n2, vslot + sj2 * SLOT, v_voff);  // slot of V_{j-1}, read last step
-      }
-      if (pending) {
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-        pending = false;
       }
       const bool has_next = STEADY || kt_n1 >= 0;
       // Region 1: Q.K^T of tile j+1 (NQK MFMAs; K fragments read three ahead) with the exp2,
@@ -387,6 +374,41 @@ __device__ __forceinline__ void attn_item(
       }
       // keep tile j's weights in this region (no sinking past the mask branch)
       keep_here(pop, ls);
+      // The weights of tile j used the running maximum m.  A row whose partial sum passes
+      // 2^70 (some weight above 2^64: the first tiles of a row, or a sharp rise of its scores)
+      // is redone with the tile's own maximum; inf and NaN sums take the same path.
+      if (__builtin_amdgcn_ballot_w64(!((ls[0] + ls[1]) + (ls[2] + ls[3]) <= 0x1p70f)) != 0) {
+        float m0 = max3f(sc[0][0], sc[1][0], sc[0][1]);
+        float m1 = max3f(sc[1][1], sc[0][2], sc[1][2]);
+#pragma unroll
+        for (int e = 3; e < 15; e += 2) {
+          m0 = max3f(m0, sc[0][e], sc[1][e]);
+          m1 = max3f(m1, sc[0][e + 1], sc[1][e + 1]);
+        }
+        const float ms = half_max(max3f(m0, m1, max3f(sc[0][15], sc[1][15], m0))) * c;
+        const float mn = fmaxf(m_sc, ms);
+        const float al = __builtin_amdgcn_exp2f(m_sc - mn);
+        m_sc = mn;
+        l_run *= al;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[db][e] *= al;
+        const float nm = -m_sc;
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ls[r] = 0.f;
+#pragma unroll
+        for (int pair = 0; pair < 16; ++pair) {
+          const int kb = pair >> 3, e = (pair & 7) * 2;
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], c, nm));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][e + 1], c, nm));
+          const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+          pop[kb][e >> 3][e & 7] = pp[0];
+          pop[kb][e >> 3][(e & 7) + 1] = pp[1];
+          ls[pair & 3] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls[pair & 3], false);
+        }
+      }
       if (!STEADY && has_next && tiles.needs_mask(kt_n1)) apply_mask(sn, kt_n1);
       // Region 2: P.V of tile j (NPV MFMAs; transposing V reads two fragments ahead) with the
       // maximum of tile j+1 placed between them.
@@ -400,21 +422,6 @@ __device__ __forceinline__ void attn_item(
           const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 8 * D));
           av[i] = __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
         };
-        float m0 = 0.f, m1 = 0.f;
-        auto max_step = [&](int st) {  // nine steps: the tile maximum of S_{j+1}, scaled
-          if (st == 0) {
-            m0 = max3f(sn[0][0], sn[1][0], sn[0][1]);
-            m1 = max3f(sn[1][1], sn[0][2], sn[1][2]);
-          } else if (st < 7) {
-            const int e = 2 * st + 1;
-            m0 = max3f(m0, sn[0][e], sn[1][e]);
-            m1 = max3f(m1, sn[0][e + 1], sn[1][e + 1]);
-          } else if (st == 7) {
-            m0 = max3f(m0, m1, max3f(sn[0][15], sn[1][15], m0));
-          } else {
-            m0 = half_max(m0) * c;
-          }
-        };
         vread(0);
         vread(1);
 #pragma unroll
@@ -422,18 +429,9 @@ __device__ __forceinline__ void attn_item(
           if (i + 2 < NPV) vread(i + 2);
           const int db = i >> 2, kb = (i >> 1) & 1, cc = i & 1;
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], pop[kb][cc], oacc[db], 0, 0, 0);
-          if (i < 9) max_step(i);
           __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int st = NPV; st < 9; ++st) max_step(st);
         l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-        if (has_next && __builtin_amdgcn_ballot_w64(m0 > m_sc + SLACK) != 0) {
-          const float mn = fmaxf(m_sc, m0);
-          alpha = __builtin_amdgcn_exp2f(m_sc - mn);
-          m_sc = mn;
-          pending = true;
-        }
       }
       const int kt_n4 = STEADY ? kt_n3 + 1 : (kt_n3 >= 0 ? tiles.next(kt_n3 + 1) : -1);
       // this step's DMA may stay in flight; the previous step's (K_{j+2}, V_{j+1}) must land
