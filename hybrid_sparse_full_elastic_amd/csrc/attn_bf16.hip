@@ -34,8 +34,8 @@
 //    and the transposing V reads are free of LDS bank conflicts.
 //  * Per tile step j, two instruction regions fenced with sched_barrier so the issue order is
 //    the written one: the Q.K^T MFMAs of tile j+1 with the exp2 / bf16 packing / row sums of
-//    tile j between them (K fragments read three MFMAs ahead), then the P.V MFMAs of tile j
-//    with the transposing V reads (two ahead) between them.  A
+//    tile j between them (K fragments read five MFMAs ahead), then the P.V MFMAs of tile j
+//    with the transposing V reads (four ahead) between them.  A
 //    wave keeps its MFMA pipe fed while its own softmax work issues beside it, and the two
 //    waves sharing a SIMD fill each other's gaps.  The mask of an edge tile sits between the
 //    regions; one barrier per step.
@@ -338,7 +338,7 @@ __device__ __forceinline__ void attn_item(
         if (kt_n2 >= 0) dma(vbase, kt_n2, vslot + sj2 * SLOT, v_voff);  // slot of V_{j-1}, read last step
       }
       const bool has_next = STEADY || kt_n1 >= 0;
-      // Region 1: Q.K^T of tile j+1 (NQK MFMAs; K fragments read three ahead) with the exp2,
+      // Region 1: Q.K^T of tile j+1 (NQK MFMAs; K fragments read five ahead) with the exp2,
       // bf16 packing and row sums of tile j placed between them.
       constexpr int NQK = 2 * DC, NPV = 4 * DB;
       constexpr int PPM = 16 / NQK;  // weight pairs per Q.K^T MFMA
@@ -351,12 +351,12 @@ __device__ __forceinline__ void attn_item(
         const f32x16 zero = {};
         bf16x8 a[NQK];
 #pragma unroll
-        for (int i = 0; i < 3; ++i)
+        for (int i = 0; i < 5; ++i)
           a[i] = *reinterpret_cast<const bf16x8*>(ks + (i & 1) * 32 * D + k_roff[i >> 1]);
 #pragma unroll
         for (int i = 0; i < NQK; ++i) {
-          if (i + 3 < NQK)
-            a[i + 3] = *reinterpret_cast<const bf16x8*>(ks + ((i + 3) & 1) * 32 * D + k_roff[(i + 3) >> 1]);
+          if (i + 5 < NQK)
+            a[i + 5] = *reinterpret_cast<const bf16x8*>(ks + ((i + 5) & 1) * 32 * D + k_roff[(i + 5) >> 1]);
           sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], qreg[i >> 1], i < 2 ? zero : sn[i & 1], 0, 0, 0);
 #pragma unroll
           for (int u = 0; u < PPM; ++u) {
@@ -410,8 +410,7 @@ __device__ __forceinline__ void attn_item(
         }
       }
       if (!STEADY && has_next && tiles.needs_mask(kt_n1)) apply_mask(sn, kt_n1);
-      // Region 2: P.V of tile j (NPV MFMAs; transposing V reads two fragments ahead) with the
-      // maximum of tile j+1 placed between them.
+      // Region 2: P.V of tile j (NPV MFMAs; transposing V reads four fragments ahead).
       {
         const uint16_t* vs = vslot + sj * SLOT;
         bf16x8 av[NPV];
@@ -424,9 +423,11 @@ __device__ __forceinline__ void attn_item(
         };
         vread(0);
         vread(1);
+        vread(2);
+        vread(3);
 #pragma unroll
         for (int i = 0; i < NPV; ++i) {
-          if (i + 2 < NPV) vread(i + 2);
+          if (i + 4 < NPV) vread(i + 4);
           const int db = i >> 2, kb = (i >> 1) & 1, cc = i & 1;
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], pop[kb][cc], oacc[db], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
