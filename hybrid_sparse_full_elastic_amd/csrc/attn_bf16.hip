@@ -61,7 +61,9 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float LN2 = 0.69314718055994530942f;
-constexpr int NSLOT = 3;  // LDS slots per operand
+constexpr int NSK = 4;   // LDS slots for K tiles
+constexpr int NSV = 3;   // LDS slots for V tiles
+constexpr int NPRE = 2;  // K fragments of the next step read before its barrier
 
 // x[lane] combined with x[lane ^ 32]; the swap returns both halves' values.
 __device__ inline float half_max(float x) {
@@ -99,8 +101,8 @@ __device__ __forceinline__ void launder_lane(int& x) { asm volatile("" : "+v"(x)
 
 template <int D>
 struct LdsTiles {
-  uint16_t k[NSLOT][BF16_BK * D];
-  uint16_t v[NSLOT][BF16_BK * D];
+  uint16_t k[NSK][BF16_BK * D];
+  uint16_t v[NSV][BF16_BK * D];
 };
 
 // XOR swizzles of the 16-byte chunk index within a tile row (D/8 chunks per row).  K is read
@@ -116,11 +118,22 @@ __device__ __host__ constexpr int v_swizzle(int row) {
   return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
+// The workgroup's claim of its next item, in LDS.  Thread 0 claims the next item during the
+// current item's prologue (the queue counter's atomic travels with the first K/V copies) and
+// loads its descriptor while the tile steps run, so no global round trip sits between two
+// items.
+struct NextClaim {
+  int idx;        // claimed item, or -1 when every queue is empty
+  int q0, len;    // this workgroup's own queue: first item and length (read once)
+  WorkItem next;  // the claimed item's descriptor
+};
+
 // One work item with its mode known at compile time.  KIND is the sparse kind of the launch:
 // each kernel instantiates its own copies of the item loops.
 template <int D, int MODE, int KIND>
 __device__ __forceinline__ void attn_item(
-    const WorkItem& it, const int tid, LdsTiles<D>& lds, uint32_t* list_vis, const uint16_t* __restrict__ q,
+    const WorkItem& it, const int tid, LdsTiles<D>& lds, uint32_t* list_vis, NextClaim& cl,
+    int32_t* sched, const WorkItem* __restrict__ items, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
     float* __restrict__ lse, const SeqGeom& geo, int Hq, int Hkv, int G, int BT, float scale_log2,
     const Pattern& pat) {
@@ -290,7 +303,9 @@ __device__ __forceinline__ void attn_item(
     m_sc = fmaxf(m_sc, half_max(max3f(m0, m1, max3f(s[0][15], s[1][15], m0))) * c);
   };
 
-  // ---- tile schedule: kt_cur = tile j, kt_n1/2/3 = tiles j+1..j+3 (-1 when absent)
+  bool claimed = false;  // uniform: the next item was claimed in the prologue
+
+  // ---- tile schedule: kt_cur = tile j, kt_n1..kt_n4 = tiles j+1..j+4 (-1 when absent)
   // An item whose queries see no key of the range (a query chunk placed before its key
   // range) skips straight to the epilogue and writes O = 0, lse = -inf.
   int kt_cur = tiles.next(0);
@@ -298,8 +313,10 @@ __device__ __forceinline__ void attn_item(
     int kt_n1 = tiles.next(kt_cur + 1);
     int kt_n2 = kt_n1 >= 0 ? tiles.next(kt_n1 + 1) : -1;
     int kt_n3 = kt_n2 >= 0 ? tiles.next(kt_n2 + 1) : -1;
+    int kt_n4 = kt_n3 >= 0 ? tiles.next(kt_n3 + 1) : -1;
 
-    // prologue: K_0..K_2 and V_0, V_1 land; S_0 computed and reduced
+    // prologue: K_0..K_3 and V_0, V_1 land; S_0 computed and reduced.  K tile j lives in K
+    // slot j mod 4, V tile j in V slot j mod 3.
     uint16_t* kslot = &lds.k[0][0];
     uint16_t* vslot = &lds.v[0][0];
     dma(kbase, kt_cur, kslot, k_voff);
@@ -309,17 +326,47 @@ __device__ __forceinline__ void attn_item(
       dma(vbase, kt_n1, vslot + SLOT, v_voff);
     }
     if (kt_n2 >= 0) dma(kbase, kt_n2, kslot + 2 * SLOT, k_voff);
+    if (kt_n3 >= 0) dma(kbase, kt_n3, kslot + 3 * SLOT, k_voff);
+    // the next item: the queue counter's atomic lands with the copies above
+    int k_next = 0;
+    if (tid == 0) k_next = atomicAdd(sched + SCHED_CTR * (1 + (int)(blockIdx.x % SCHED_NX)), 1);
     WAIT_VMCNT(0);
-    __syncthreads();
+    __syncthreads();  // every wave has read this item's claim: the slot is free
+    if (wave == 0) {
+      int idx = 0;
+      if (tid == 0) {
+        idx = k_next < cl.len ? cl.q0 + k_next : claim_item(sched);
+        cl.idx = idx;
+      }
+      idx = __builtin_amdgcn_readfirstlane(idx);
+      // its descriptor goes global -> LDS by DMA (4 lanes x 4 bytes) and lands during the
+      // tile steps, whose copy waits retire it
+      if (idx >= 0 && lane < 4) {
+        const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<WorkItem*>(items + idx), (short)0,
+                                                          (int)sizeof(WorkItem), 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)&cl.next, 4, lane * 4, 0, 0, 0);
+      }
+    }
+    claimed = true;
     f32x16 s0[2], s1[2];
     qk(kslot, s0);
     __syncthreads();  // every wave is done with K slot 0 before step 0 refills it
     if (tiles.needs_mask(kt_cur)) apply_mask(s0, kt_cur);
     first_max(s0);
-    int sj = 0;       // LDS slot of tile j (tile t lives in slot t mod 3)
+    int skj = 0, svj = 0;  // LDS slots of K_j and V_j
+    // the first K fragments of step 0 (tile 1)
+    bf16x8 kpre[NPRE];
+#pragma unroll
+    for (int i = 0; i < NPRE; ++i)
+      kpre[i] = *reinterpret_cast<const bf16x8*>(kslot + SLOT + (i & 1) * 32 * D + k_roff[i >> 1]);
 
-    // One step on tile j: DMA K_{j+3} and V_{j+2}; S_{j+1} = K_{j+1} Q^T; p_j = exp2(c s_j - m);
-    // O += V_j^T P_j^T; mask and maximum of S_{j+1}; wait for the previous step's DMA; barrier.
+    // One step on tile j: DMA K_{j+4} and V_{j+2}; S_{j+1} = K_{j+1} Q^T; p_j = exp2(c s_j - m);
+    // O += V_j^T P_j^T; the first K fragments of tile j+2; mask of S_{j+1}; wait for the
+    // previous step's DMA; barrier.
+    // Slots: K_{j+4} refills the slot of K_j (read last step), V_{j+2} that of V_{j-1} (read
+    // last step).  K_{j+2} landed before the previous barrier (it was copied two steps ago), so
+    // its first fragments are read before this step's barrier and the next step's first
+    // MFMAs wait for no LDS read.
     // STEADY: a step inside a run of consecutive whole tiles where tile j+1 needs no mask (the
     // key-tile schedule's steady_pair), so no bound, mask or DMA-count decisions are taken:
     // the scalar work of a step shrinks to the DMA descriptors and one loop test.  Used for
@@ -327,36 +374,33 @@ __device__ __forceinline__ void attn_item(
     // sparse items the extra loop copy costs more than it saves.
     auto step = [&](auto steady_tag, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
       constexpr bool STEADY = decltype(steady_tag)::value;
-      const int sj1 = sj == NSLOT - 1 ? 0 : sj + 1;
-      const int sj2 = sj1 == NSLOT - 1 ? 0 : sj1 + 1;
-      const int n_dma = STEADY ? 2 * CPT : (kt_n3 >= 0 ? CPT : 0) + (kt_n2 >= 0 ? CPT : 0);
-      if (STEADY) {
-        dma_full(kbase, kt_n3, kslot + sj * SLOT, k_voff);
-        dma_full(vbase, kt_n2, vslot + sj2 * SLOT, v_voff);
-      } else {
-        if (kt_n3 >= 0) dma(kbase, kt_n3, kslot + sj * SLOT, k_voff);   // slot of K_j, read last step
-        if (kt_n2 >= 0) dma(vbase, kt_n2, vslot + sj2 * SLOT, v_voff);  // slot of V_{j-1}, read last step
-      }
+      const int sk1 = (skj + 1) & (NSK - 1), sk2 = (skj + 2) & (NSK - 1);
+      const int sv2 = svj == 0 ? NSV - 1 : svj - 1;
+      const int n_dma = STEADY ? 2 * CPT : (kt_n4 >= 0 ? CPT : 0) + (kt_n2 >= 0 ? CPT : 0);
       const bool has_next = STEADY || kt_n1 >= 0;
       // Region 1: Q.K^T of tile j+1 (NQK MFMAs; K fragments read five ahead) with the exp2,
-      // bf16 packing and row sums of tile j placed between them.
+      // bf16 packing and row sums of tile j placed between them; the DMA is issued after the
+      // first MFMAs.
       constexpr int NQK = 2 * DC, NPV = 4 * DB;
       constexpr int PPM = 16 / NQK;  // weight pairs per Q.K^T MFMA
+      constexpr int AHEAD = 5;
       bf16x8 pop[2][2];
       float ls[4] = {0.f, 0.f, 0.f, 0.f};
       {
-        const uint16_t* ks = kslot + sj1 * SLOT;
+        const uint16_t* ks = kslot + sk1 * SLOT;
         const float nm = -m_sc;
         const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
         const f32x16 zero = {};
         bf16x8 a[NQK];
 #pragma unroll
-        for (int i = 0; i < 5; ++i)
+        for (int i = 0; i < NPRE; ++i) a[i] = kpre[i];
+#pragma unroll
+        for (int i = NPRE; i < AHEAD; ++i)
           a[i] = *reinterpret_cast<const bf16x8*>(ks + (i & 1) * 32 * D + k_roff[i >> 1]);
 #pragma unroll
         for (int i = 0; i < NQK; ++i) {
-          if (i + 5 < NQK)
-            a[i + 5] = *reinterpret_cast<const bf16x8*>(ks + ((i + 5) & 1) * 32 * D + k_roff[(i + 5) >> 1]);
+          if (i + AHEAD < NQK)
+            a[i + AHEAD] = *reinterpret_cast<const bf16x8*>(ks + ((i + AHEAD) & 1) * 32 * D + k_roff[(i + AHEAD) >> 1]);
           sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], qreg[i >> 1], i < 2 ? zero : sn[i & 1], 0, 0, 0);
 #pragma unroll
           for (int u = 0; u < PPM; ++u) {
@@ -368,6 +412,15 @@ __device__ __forceinline__ void attn_item(
             pop[kb][e >> 3][e & 7] = pp[0];
             pop[kb][e >> 3][(e & 7) + 1] = pp[1];
             ls[pair & 3] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls[pair & 3], false);
+          }
+          if (i == 1) {
+            if (STEADY) {
+              dma_full(kbase, kt_n4, kslot + skj * SLOT, k_voff);
+              dma_full(vbase, kt_n2, vslot + sv2 * SLOT, v_voff);
+            } else {
+              if (kt_n4 >= 0) dma(kbase, kt_n4, kslot + skj * SLOT, k_voff);
+              if (kt_n2 >= 0) dma(vbase, kt_n2, vslot + sv2 * SLOT, v_voff);
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -412,7 +465,8 @@ __device__ __forceinline__ void attn_item(
       if (!STEADY && has_next && tiles.needs_mask(kt_n1)) apply_mask(sn, kt_n1);
       // Region 2: P.V of tile j (NPV MFMAs; transposing V reads four fragments ahead).
       {
-        const uint16_t* vs = vslot + sj * SLOT;
+        const uint16_t* vs = vslot + svj * SLOT;
+        const uint16_t* kn = kslot + sk2 * SLOT;
         bf16x8 av[NPV];
         auto vread = [&](int i) {
           const int db = i >> 2, kb = (i >> 1) & 1, cc = i & 1;
@@ -430,11 +484,15 @@ __device__ __forceinline__ void attn_item(
           if (i + 4 < NPV) vread(i + 4);
           const int db = i >> 2, kb = (i >> 1) & 1, cc = i & 1;
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], pop[kb][cc], oacc[db], 0, 0, 0);
+          // the first K fragments of tile j+2, after the last V reads
+          if (i >= NPV - NPRE)
+            kpre[i - (NPV - NPRE)] =
+                *reinterpret_cast<const bf16x8*>(kn + ((i - (NPV - NPRE)) & 1) * 32 * D + k_roff[(i - (NPV - NPRE)) >> 1]);
           __builtin_amdgcn_sched_barrier(0);
         }
         l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
       }
-      const int kt_n4 = STEADY ? kt_n3 + 1 : (kt_n3 >= 0 ? tiles.next(kt_n3 + 1) : -1);
+      const int kt_n5 = STEADY ? kt_n4 + 1 : (kt_n4 >= 0 ? tiles.next(kt_n4 + 1) : -1);
       // this step's DMA may stay in flight; the previous step's (K_{j+2}, V_{j+1}) must land
       if (n_dma == 2 * CPT) WAIT_VMCNT(2 * CPT);
       else if (n_dma == CPT) WAIT_VMCNT(CPT);
@@ -446,14 +504,16 @@ __device__ __forceinline__ void attn_item(
       kt_n1 = kt_n2;
       kt_n2 = kt_n3;
       kt_n3 = kt_n4;
-      sj = sj1;
+      kt_n4 = kt_n5;
+      skj = sk1;
+      svj = svj == NSV - 1 ? 0 : svj + 1;
     };
 
     using SteadyT = std::integral_constant<bool, true>;
     using GeneralT = std::integral_constant<bool, false>;
     if (MODE == MODE_FULL) {
       // Full items visit consecutive tiles.  A pair of steady steps from tile j loads tiles up
-      // to j+4 (whole inside the key range), advances the schedule to j+5 (a visited tile) and
+      // to j+5 (whole inside the key range), advances the schedule to j+6 (a visited tile) and
       // computes S of tiles j+1, j+2 (below the diagonal and the key range's end: no mask).
       while (tiles.steady_pair(kt_cur)) {
         step(SteadyT{}, s0, s1);
@@ -465,6 +525,17 @@ __device__ __forceinline__ void attn_item(
       if (kt_cur < 0) break;
       step(GeneralT{}, s1, s0);
       if (kt_cur < 0) break;
+    }
+  }
+
+  // ---- the next item, for an item without keys (no prologue ran): claim it now, once every
+  // wave has read this item's claim
+  if (!claimed) {
+    __syncthreads();
+    if (tid == 0) {
+      const int idx = claim_item(sched);
+      cl.idx = idx;
+      if (idx >= 0) cl.next = items[idx];
     }
   }
 
@@ -510,7 +581,6 @@ struct AttnArgs {
   SeqGeom geo;
   int Hq, Hkv, G, BT;
   float scale_log2;
-  const int32_t* head_mask;
   Pattern pat;
   const WorkItem* items;
   int32_t* sched;
@@ -525,7 +595,7 @@ template <int D, bool LISTS>
 struct __attribute__((aligned(1024))) KernelLds {
   LdsTiles<D> tiles;
   uint32_t list_vis[LISTS ? LIST_MAX_KB : 1];  // block lists: visibility per key block
-  int claim;                                    // the item claimed for the workgroup
+  NextClaim claim;                              // the workgroup's next item
 };
 
 // One kernel per sparse pattern kind: every launch holds full items and items of one sparse
@@ -542,18 +612,30 @@ __global__ __launch_bounds__(BF16_NW * 64, 1) void attn_bf16_kernel(AttnArgs arg
   // whole loop (which spills).  (Taking the address of `args` would copy it to scratch.)
   ConstArgs* const base = (ConstArgs*)__builtin_amdgcn_kernarg_segment_ptr();
   if (base->sched != args.sched || base->items != args.items) return;  // layout as assumed
+  if (threadIdx.x == 0) {  // the first claim; later ones come from each item's prologue
+    const int x = (int)(blockIdx.x % SCHED_NX);
+    shm.claim.q0 = base->sched[1 + x];
+    shm.claim.len = base->sched[2 + x] - shm.claim.q0;
+    const int idx = claim_item(base->sched);
+    shm.claim.idx = idx;
+    if (idx >= 0) shm.claim.next = base->items[idx];
+  }
   for (;;) {
     ConstArgs* a = base;
     launder(a);
-    if (threadIdx.x == 0) shm.claim = claim_item(a->sched);
+    // the claim is in LDS, and every wave is done with the previous item's LDS (O staging)
     lds_wait_barrier();
-    // uniform, and in a scalar register
-    const int idx = __builtin_amdgcn_readfirstlane(shm.claim);
+    // uniform, and in scalar registers
+    const int idx = __builtin_amdgcn_readfirstlane(shm.claim.idx);
     if (idx < 0) return;  // every queue is empty
-    const WorkItem it = a->items[idx];
+    WorkItem it;
+    it.seq = __builtin_amdgcn_readfirstlane(shm.claim.next.seq);
+    it.group = __builtin_amdgcn_readfirstlane(shm.claim.next.group);
+    it.qtile = __builtin_amdgcn_readfirstlane(shm.claim.next.qtile);
+    it.full = __builtin_amdgcn_readfirstlane(shm.claim.next.full);
     int tid = threadIdx.x;
     launder_lane(tid);
-    const bool full = a->head_mask == nullptr || a->head_mask[it.seq * a->Hkv + it.group] != 0;
+    const bool full = it.full != 0;
     SeqGeom geo;
     geo.cu_q = a->geo.cu_q, geo.cu_k = a->geo.cu_k, geo.total_q = a->geo.total_q;
     geo.total_k = a->geo.total_k, geo.q_pos = a->geo.q_pos, geo.k_pos = a->geo.k_pos;
@@ -562,7 +644,8 @@ __global__ __launch_bounds__(BF16_NW * 64, 1) void attn_bf16_kernel(AttnArgs arg
     pat.block = a->pat.block, pat.sink_blocks = a->pat.sink_blocks;
     pat.local_blocks = a->pat.local_blocks, pat.stride_blocks = a->pat.stride_blocks;
     pat.qblocks = a->pat.qblocks, pat.row_ptr = a->pat.row_ptr, pat.col_idx = a->pat.col_idx;
-#define ELASTIC_ITEM_ARGS it, tid, shm.tiles, shm.list_vis, a->q, a->k, a->v, a->o, a->lse, geo, \
+#define ELASTIC_ITEM_ARGS it, tid, shm.tiles, shm.list_vis, shm.claim, a->sched, a->items, a->q, \
+                          a->k, a->v, a->o, a->lse, geo, \
                           a->Hq, a->Hkv, a->G, a->BT, a->scale_log2, pat
     if (full)
       attn_item<D, MODE_FULL, KIND>(ELASTIC_ITEM_ARGS);
@@ -573,9 +656,6 @@ __global__ __launch_bounds__(BF16_NW * 64, 1) void attn_bf16_kernel(AttnArgs arg
     else
       attn_item<D, MODE_LIST, KIND>(ELASTIC_ITEM_ARGS);
 #undef ELASTIC_ITEM_ARGS
-    // every wave is done with the LDS tiles (O staging) and with the claim slot before the
-    // next claim
-    lds_wait_barrier();
   }
 }
 
@@ -596,7 +676,7 @@ hipError_t launch_attn_bf16(int head_dim, const void* q, const void* k, const vo
     if (err != hipSuccess) return;
     grid = grid < max_items ? grid : max_items;
     const AttnArgs args{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
-                        geo, n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask, pat, items, sched};
+                        geo, n_q_heads, n_kv_heads, G, BT, scale_log2, pat, items, sched};
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(BF16_NW * 64), 0, stream, args);
   };
   // without a head mask every item is full: any instantiation serves

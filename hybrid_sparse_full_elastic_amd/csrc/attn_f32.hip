@@ -20,7 +20,7 @@ template <int D>
 __global__ __launch_bounds__(F32_ROWS, 1) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, float* __restrict__ lse, SeqGeom geo, int Hq, int Hkv, int G, int BT,
-    float scale_log2, const int32_t* __restrict__ head_mask, Pattern pat,
+    float scale_log2, Pattern pat,
     const WorkItem* __restrict__ items, int32_t* sched) {
   constexpr int BK = F32_BK, NT = F32_ROWS;
   constexpr int CH = BK * D / 4;  // float4 chunks per tile
@@ -42,7 +42,7 @@ __global__ __launch_bounds__(F32_ROWS, 1) void attn_f32_kernel(
   const int t0 = it.qtile * BT;
   const int t1 = min(t0 + BT, n) - 1;
   const int g = it.group;
-  const bool full = head_mask == nullptr || head_mask[it.seq * Hkv + g] != 0;
+  const bool full = it.full != 0;
   const int mode = full ? MODE_FULL : pat.kind;
   const int k_end = geo.k_pos + sp.nk;
 
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(F32_ROWS, 1) void attn_f32_kernel(
 
 hipError_t launch_attn_f32(int head_dim, const void* q, const void* k, const void* v, void* o,
                            float* lse, const SeqGeom& geo, int n_q_heads, int n_kv_heads, int BT,
-                           float scale, const int32_t* head_mask, const Pattern& pat,
+                           float scale, const Pattern& pat,
                            const WorkItem* items, int32_t* sched, int64_t grid,
                            hipStream_t stream) {
   const float scale_log2 = scale * 1.4426950408889634f;
@@ -156,11 +156,11 @@ hipError_t launch_attn_f32(int head_dim, const void* q, const void* k, const voi
   if (head_dim == 128) {
     hipLaunchKernelGGL(attn_f32_kernel<128>, dim3((unsigned)grid), dim3(F32_ROWS), 0, stream,
                        (const float*)q, (const float*)k, (const float*)v, (float*)o, lse, geo,
-                       n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask, pat, items, sched);
+                       n_q_heads, n_kv_heads, G, BT, scale_log2, pat, items, sched);
   } else {
     hipLaunchKernelGGL(attn_f32_kernel<64>, dim3((unsigned)grid), dim3(F32_ROWS), 0, stream,
                        (const float*)q, (const float*)k, (const float*)v, (float*)o, lse, geo,
-                       n_q_heads, n_kv_heads, G, BT, scale_log2, head_mask, pat, items, sched);
+                       n_q_heads, n_kv_heads, G, BT, scale_log2, pat, items, sched);
   }
   return hipGetLastError();
 }

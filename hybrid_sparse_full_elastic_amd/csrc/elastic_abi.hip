@@ -303,7 +303,7 @@ int attn_call(const char* who, const void* q, const void* k, const void* v, void
                          head_mask, pat, items, sched, max_items, st);
   else
     e = launch_attn_f32(head_dim, q, k, v, o, lse_out, geo, n_q_heads, n_kv_heads, BT, scale,
-                        head_mask, pat, items, sched, max_items, st);
+                        pat, items, sched, max_items, st);
   if (e != hipSuccess) {
     snprintf(where, sizeof(where), "%s: attention", who);
     return hip_fail(e, where);

@@ -152,7 +152,7 @@ struct WorkItem {
   int seq;    // sequence index b
   int group;  // KV head g
   int qtile;  // query tile index: tokens [qtile * BT, min(n, (qtile + 1) * BT))
-  int cost;   // key tiles visited (scheduling weight)
+  int full;   // 1: the KV head runs full attention, 0: its sparse pattern (from the head mask)
 };
 
 // Is key j visible to query i (local positions) under `mode`?
@@ -279,16 +279,17 @@ struct KeyTilesT {
     return last < lo ? 0 : cnt_upto(last) - cnt_upto(lo - 1);
   }
 
-  // May a pair of steady steps start at visited tile j?  Then tiles j..j+5 are visited
-  // consecutively, tiles j..j+4 hold BK keys of the range each, and tiles j+1, j+2 need no
-  // mask: the pair loads, computes and advances without any bound decision.  Such runs are
+  // May a pair of steady steps start at visited tile j?  Then tiles j..j+6 are visited
+  // consecutively, tiles j..j+5 hold BK keys of the range each, and tiles j+1, j+2 need no
+  // mask: the pair loads (K up to tile j+5), computes and advances (the schedule looks six
+  // tiles ahead) without any bound decision.  Such runs are
   // a full item's tiles below the diagonal, a streaming item's window interior, and the
   // local blocks every query of a block item sees.
   __host__ __device__ bool steady_pair(int j) const {
     const int whole_end = k_end / BK;
     const int causal = (t0 + 1) / BK;  // tiles below hold only keys <= t0
     const int mask_from = causal < whole_end ? causal : whole_end;
-    if (!(j + 5 <= last && j + 4 < whole_end && j + 2 < mask_from)) return false;
+    if (!(j + 6 <= last && j + 5 < whole_end && j + 2 < mask_from)) return false;
     if (mode() == MODE_FULL) return true;
     if (mode() == MODE_STREAM) return j >= win_begin && (j + 1) * BK > t1 - p.window;
     const int run = (qb0 - p.local_blocks > 0 ? qb0 - p.local_blocks : 0) * tpb;
@@ -361,7 +362,7 @@ hipError_t launch_attn_bf16(int head_dim, const void* q, const void* k, const vo
 
 hipError_t launch_attn_f32(int head_dim, const void* q, const void* k, const void* v, void* o,
                            float* lse, const SeqGeom& geo, int n_q_heads, int n_kv_heads, int BT,
-                           float scale, const int32_t* head_mask, const Pattern& pat,
+                           float scale, const Pattern& pat,
                            const WorkItem* items, int32_t* sched, int64_t max_items,
                            hipStream_t stream);
 

@@ -232,9 +232,11 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     WorkItem it;
     locate(u, it);
     const int packed = cost[u];
-    it.cost = packed & 0x0fffffff;
+    const int c = packed & 0x0fffffff;
     const int x = (int)((unsigned)packed >> 28);
-    items[atomicAdd(&hist[x * PLAN_BUCKETS + (PLAN_BUCKETS - 1 - bucket_of(it.cost))], 1)] = it;
+    const int mi = it.seq * n_kv_heads + it.group;
+    it.full = (mask_cached ? s_full[mi] != 0 : (head_mask == nullptr || head_mask[mi] != 0)) ? 1 : 0;
+    items[atomicAdd(&hist[x * PLAN_BUCKETS + (PLAN_BUCKETS - 1 - bucket_of(c))], 1)] = it;
   }
   if (tid == 0) {
     sched[0] = nitem;

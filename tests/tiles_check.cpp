@@ -56,9 +56,9 @@ int main() {
               for (int j = kt.next(0); j >= 0; j = kt.next(j + 1)) {
                 if (!kt.steady_pair(j)) continue;
                 ++steady;
-                for (int i = 1; i <= 5; ++i)
+                for (int i = 1; i <= 6; ++i)
                   if (kt.next(j + i) != j + i) fail("steady-next", mode, t0, t1, BK, j + i);
-                if ((j + 5) * BK > ke) fail("steady-whole", mode, t0, t1, BK, j);
+                if ((j + 6) * BK > ke) fail("steady-whole", mode, t0, t1, BK, j);
                 if (kt.needs_mask(j + 1) || kt.needs_mask(j + 2)) fail("steady-mask", mode, t0, t1, BK, j);
               }
               // the compile-time-mode instances walk the same tiles
