@@ -64,6 +64,7 @@ constexpr float LN2 = 0.69314718055994530942f;
 constexpr int NSK = 4;   // LDS slots for K tiles
 constexpr int NSV = 3;   // LDS slots for V tiles
 constexpr int NPRE = 2;  // K fragments of the next step read before its barrier
+constexpr int NVPRE = 2; // V fragments of a step read during its Q.K^T MFMAs
 
 // x[lane] combined with x[lane ^ 32]; the swap returns both halves' values.
 __device__ inline float half_max(float x) {
@@ -379,13 +380,24 @@ __device__ __forceinline__ void attn_item(
       const int n_dma = STEADY ? 2 * CPT : (kt_n4 >= 0 ? CPT : 0) + (kt_n2 >= 0 ? CPT : 0);
       const bool has_next = STEADY || kt_n1 >= 0;
       // Region 1: Q.K^T of tile j+1 (NQK MFMAs; K fragments read five ahead) with the exp2,
-      // bf16 packing and row sums of tile j placed between them; the DMA is issued after the
-      // first MFMAs.
+      // bf16 packing and row sums of tile j placed between them; the DMA is issued halfway
+      // (measured: 1.6% faster on full heads than right after the first MFMAs), and the
+      // first V fragments of region 2 are read during the last MFMAs.
       constexpr int NQK = 2 * DC, NPV = 4 * DB;
       constexpr int PPM = 16 / NQK;  // weight pairs per Q.K^T MFMA
       constexpr int AHEAD = 5;
       bf16x8 pop[2][2];
       float ls[4] = {0.f, 0.f, 0.f, 0.f};
+      // transposing reads of V_j (landed before the last barrier)
+      const uint16_t* vs = vslot + svj * SLOT;
+      bf16x8 av[NPV];
+      auto vread = [&](int i) {
+        const int db = i >> 2, kb = (i >> 1) & 1, cc = i & 1;
+        const uint16_t* src = vs + v_roff[db] + (kb * 32 + cc * 16) * D;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 8 * D));
+        av[i] = __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      };
       {
         const uint16_t* ks = kslot + sk1 * SLOT;
         const float nm = -m_sc;
@@ -413,7 +425,9 @@ __device__ __forceinline__ void attn_item(
             pop[kb][e >> 3][(e & 7) + 1] = pp[1];
             ls[pair & 3] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls[pair & 3], false);
           }
-          if (i == 1) {
+          // the first V fragments of region 2, during the last MFMAs
+          if (i >= NQK - NVPRE) vread(i - (NQK - NVPRE));
+          if (i == NQK / 2) {
             if (STEADY) {
               dma_full(kbase, kt_n4, kslot + skj * SLOT, k_voff);
               dma_full(vbase, kt_n2, vslot + sv2 * SLOT, v_voff);
@@ -465,20 +479,9 @@ __device__ __forceinline__ void attn_item(
       if (!STEADY && has_next && tiles.needs_mask(kt_n1)) apply_mask(sn, kt_n1);
       // Region 2: P.V of tile j (NPV MFMAs; transposing V reads four fragments ahead).
       {
-        const uint16_t* vs = vslot + svj * SLOT;
         const uint16_t* kn = kslot + sk2 * SLOT;
-        bf16x8 av[NPV];
-        auto vread = [&](int i) {
-          const int db = i >> 2, kb = (i >> 1) & 1, cc = i & 1;
-          const uint16_t* src = vs + v_roff[db] + (kb * 32 + cc * 16) * D;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 8 * D));
-          av[i] = __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-        };
-        vread(0);
-        vread(1);
-        vread(2);
-        vread(3);
+#pragma unroll
+        for (int i = NVPRE; i < 4; ++i) vread(i);
 #pragma unroll
         for (int i = 0; i < NPV; ++i) {
           if (i + 4 < NPV) vread(i + 4);
@@ -493,7 +496,7 @@ __device__ __forceinline__ void attn_item(
         l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
       }
       const int kt_n5 = STEADY ? kt_n4 + 1 : (kt_n4 >= 0 ? tiles.next(kt_n4 + 1) : -1);
-      // this step's DMA may stay in flight; the previous step's (K_{j+2}, V_{j+1}) must land
+      // this step's DMA may stay in flight; the previous step's (K_{j+3}, V_{j+1}) must land
       if (n_dma == 2 * CPT) WAIT_VMCNT(2 * CPT);
       else if (n_dma == CPT) WAIT_VMCNT(CPT);
       else WAIT_VMCNT(0);
