@@ -273,14 +273,25 @@ __device__ __forceinline__ void attn_item(
     } else if (MODE == MODE_LIST) {
       b = tiles.lists(kt, qblk) ? 0 : 0x7fffffff;
     }
-    const int base = kt * BK + half * 4;
+    // This lane's keys of the tile as bits (offset o = j - kt*BK): [0, hi] minus [a, b), one 32-bit
+    // word per 32-key half, shifted so that element (kb, e) sits at bit (e/4)*8 + e%4.  Each
+    // element then takes one sign-extending bit extract and one bitwise select (no compares,
+    // no branches).
+    const int base = kt * BK;
+    auto low_bits = [](int n) -> uint32_t { return n >= 32 ? 0xffffffffu : (n <= 0 ? 0u : (1u << n) - 1u); };
+    // interval ends, exclusive; keys are >= 0, so b <= 0 means no gap (and no overflow below)
+    const int A = a - base, B = (b > 0 ? b : 0) - base, H = hi + 1 - base;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      const int o = kb * 32;
+      const uint32_t w = (low_bits(H - o) & (low_bits(A - o) | ~low_bits(B - o))) >> (half * 4);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int j = base + kb * 32 + (e >> 2) * 8 + (e & 3);
-        if (!(j <= hi && (j < a || j >= b))) s[kb][e] = -__builtin_huge_valf();
+        const uint32_t keep = (uint32_t)__builtin_amdgcn_sbfe((int)w, (e >> 2) * 8 + (e & 3), 1);
+        const uint32_t x = __float_as_uint(s[kb][e]);
+        s[kb][e] = __uint_as_float((x & keep) | (0xff800000u & ~keep));  // -inf where masked
       }
+    }
   };
 
   // ---- running state (m in the scaled log2 domain)
@@ -317,41 +328,46 @@ __device__ __forceinline__ void attn_item(
     int kt_n4 = kt_n3 >= 0 ? tiles.next(kt_n3 + 1) : -1;
 
     // prologue: K_0..K_3 and V_0, V_1 land; S_0 computed and reduced.  K tile j lives in K
-    // slot j mod 4, V tile j in V slot j mod 3.
+    // slot j mod 4, V tile j in V slot j mod 3.  Only Q and K_0 are waited for before S_0;
+    // the other copies land while it is computed.
     uint16_t* kslot = &lds.k[0][0];
     uint16_t* vslot = &lds.v[0][0];
-    dma(kbase, kt_cur, kslot, k_voff);
-    dma(vbase, kt_cur, vslot, v_voff);
-    if (kt_n1 >= 0) {
-      dma(kbase, kt_n1, kslot + SLOT, k_voff);
-      dma(vbase, kt_n1, vslot + SLOT, v_voff);
-    }
-    if (kt_n2 >= 0) dma(kbase, kt_n2, kslot + 2 * SLOT, k_voff);
-    if (kt_n3 >= 0) dma(kbase, kt_n3, kslot + 3 * SLOT, k_voff);
-    // the next item: the queue counter's atomic lands with the copies above
+    // the next item: the queue counter's atomic goes first and lands with K_0
     int k_next = 0;
     if (tid == 0) k_next = atomicAdd(sched + SCHED_CTR * (1 + (int)(blockIdx.x % SCHED_NX)), 1);
+    dma(kbase, kt_cur, kslot, k_voff);
+    if (kt_n1 >= 0) dma(kbase, kt_n1, kslot + SLOT, k_voff);
+    dma(vbase, kt_cur, vslot, v_voff);
+    if (kt_n2 >= 0) dma(kbase, kt_n2, kslot + 2 * SLOT, k_voff);
+    if (kt_n1 >= 0) dma(vbase, kt_n1, vslot + SLOT, v_voff);
+    if (kt_n3 >= 0) dma(kbase, kt_n3, kslot + 3 * SLOT, k_voff);
+    // copies issued after K_0 (each CPT instructions): V_0, and K_1, V_1, K_2, K_3 if present
+    const int n_after = 1 + (kt_n1 >= 0 ? 2 : 0) + (kt_n2 >= 0 ? 1 : 0) + (kt_n3 >= 0 ? 1 : 0);
+    if (n_after == 5) WAIT_VMCNT(5 * CPT);
+    else if (n_after == 4) WAIT_VMCNT(4 * CPT);
+    else if (n_after == 3) WAIT_VMCNT(3 * CPT);
+    else WAIT_VMCNT(CPT);
+    __syncthreads();  // K_0 is in LDS, and every wave has read this item's claim: the slot is free
+    int next_idx = 0;  // thread 0
+    if (tid == 0) {
+      next_idx = k_next < cl.len ? cl.q0 + k_next : claim_item(sched);
+      cl.idx = next_idx;
+    }
+    claimed = true;
+    f32x16 s0[2], s1[2];
+    qk(kslot, s0);
     WAIT_VMCNT(0);
-    __syncthreads();  // every wave has read this item's claim: the slot is free
+    __syncthreads();  // every copy has landed, and every wave is done with K slot 0 before step 0 refills it
     if (wave == 0) {
-      int idx = 0;
-      if (tid == 0) {
-        idx = k_next < cl.len ? cl.q0 + k_next : claim_item(sched);
-        cl.idx = idx;
-      }
-      idx = __builtin_amdgcn_readfirstlane(idx);
-      // its descriptor goes global -> LDS by DMA (4 lanes x 4 bytes) and lands during the
-      // tile steps, whose copy waits retire it
+      // the next item's descriptor goes global -> LDS by DMA (4 lanes x 4 bytes) and lands
+      // during the tile steps, whose copy waits retire it
+      const int idx = __builtin_amdgcn_readfirstlane(next_idx);
       if (idx >= 0 && lane < 4) {
         const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<WorkItem*>(items + idx), (short)0,
                                                           (int)sizeof(WorkItem), 0x00020000);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)&cl.next, 4, lane * 4, 0, 0, 0);
       }
     }
-    claimed = true;
-    f32x16 s0[2], s1[2];
-    qk(kslot, s0);
-    __syncthreads();  // every wave is done with K slot 0 before step 0 refills it
     if (tiles.needs_mask(kt_cur)) apply_mask(s0, kt_cur);
     first_max(s0);
     int skj = 0, svj = 0;  // LDS slots of K_j and V_j
