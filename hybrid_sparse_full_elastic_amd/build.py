@@ -20,10 +20,15 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libelastic.so")
 ARCH = "gfx950"
 
-# Packed fp32 VALU instructions are disabled for every device compile.
+# Packed fp32 VALU instructions are disabled for every device compile.  The atomic optimizer
+# is off: it rewrites a one-lane atomic into a wave-level one whose result is consumed (with a
+# wait on every outstanding load) right after it, which would serialise the attention prologue
+# behind its work-queue claim.  The other atomics here are single-lane or go to lane-dependent
+# addresses, which the optimizer does not rewrite.
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     f"-I{INCLUDE}",
 ]
 

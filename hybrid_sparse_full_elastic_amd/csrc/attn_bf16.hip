@@ -129,6 +129,29 @@ struct NextClaim {
   WorkItem next;  // the claimed item's descriptor
 };
 
+// The Q fragments of one item: lane (l32, half) of wave w holds row r = w*32 + l32 (token
+// r / G, head r % G of the item's KV group), elements dc*16 + half*8 .. +7 in qreg[dc]; rows
+// past the item's tokens are zero.
+template <int D>
+__device__ __forceinline__ void load_q(bf16x8 (&qreg)[D / 16], const uint16_t* __restrict__ q,
+                                       const SeqGeom& geo, const WorkItem& it, int tid, int Hq, int G,
+                                       int BT) {
+  const SeqSpan sp = seq_span(geo, it.seq);
+  const int lane = tid & 63, r = (tid >> 6) * 32 + (lane & 31), half = lane >> 5;
+  const int tl = r / G;
+  const int t0 = it.qtile * BT;
+  const int qi = t0 + tl;
+  if (tl < BT && qi <= min(t0 + BT, sp.nq) - 1) {
+    const int qhead = it.group * G + (r - tl * G);
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + ((sp.q0 + qi) * Hq + qhead) * (int64_t)D + half * 8);
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) qreg[dc] = __builtin_bit_cast(bf16x8, src[dc * 2]);
+  } else {
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) qreg[dc] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+  }
+}
+
 // One work item with its mode known at compile time.  KIND is the sparse kind of the launch:
 // each kernel instantiates its own copies of the item loops.
 template <int D, int MODE, int KIND>
@@ -181,14 +204,7 @@ __device__ __forceinline__ void attn_item(
   const bool qvalid = tl < BT && qi <= t1;
   const int qblk = qabs >> blk_shift;
   bf16x8 qreg[DC];
-  if (qvalid) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(q + ((seq0 + qi) * Hq + qhead) * (int64_t)D + half * 8);
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) qreg[dc] = __builtin_bit_cast(bf16x8, src[dc * 2]);
-  } else {
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) qreg[dc] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-  }
+  load_q<D>(qreg, q, geo, it, tid, Hq, G, BT);
 
   // ---- DMA staging.  Instruction m of wave w fills LDS chunks [(w*CPT+m)*64, +64) of a tile;
   // lane i's chunk P holds row P/CPR, logical chunk (P%CPR) ^ swizzle(row).
@@ -356,8 +372,12 @@ __device__ __forceinline__ void attn_item(
     claimed = true;
     f32x16 s0[2], s1[2];
     qk(kslot, s0);
-    WAIT_VMCNT(0);
-    __syncthreads();  // every copy has landed, and every wave is done with K slot 0 before step 0 refills it
+    // every copy but V_1 and K_3 (first read in step 1; step 0's closing wait retires them) has
+    // landed, and every wave is done with K slot 0 before step 0 refills it
+    if (kt_n3 >= 0) WAIT_VMCNT(2 * CPT);
+    else if (kt_n1 >= 0) WAIT_VMCNT(CPT);
+    else WAIT_VMCNT(0);
+    __syncthreads();
     if (wave == 0) {
       // the next item's descriptor goes global -> LDS by DMA (4 lanes x 4 bytes) and lands
       // during the tile steps, whose copy waits retire it
