@@ -179,6 +179,10 @@ struct KeyTilesT {
   Pattern p;
   int sink_end, win_begin;  // streaming: tiles [0, sink_end) and [win_begin, diag]
   int tpb, qb0, qb1;        // block: tiles per block, query blocks of t0 and t1
+  // block: log2 of tiles per block and of the block size (both powers of two), and
+  // stride_blocks - 1 when the stride is a power of two (else -1): the per-step tile walk
+  // then takes shifts and masks instead of scalar divisions
+  int tpb_shift, blk_shift, stride_mask;
 
   __host__ __device__ int mode() const { return M >= 0 ? M : mode_rt; }
 
@@ -194,6 +198,8 @@ struct KeyTilesT {
     win_begin = 0;
     tpb = 1;
     qb0 = qb1 = 0;
+    tpb_shift = blk_shift = 0;
+    stride_mask = -1;
     if (mode() == MODE_STREAM) {
       const int sink_keys = p.sink < t1 + 1 ? p.sink : t1 + 1;
       sink_end = (sink_keys + BK - 1) / BK;
@@ -203,6 +209,9 @@ struct KeyTilesT {
       tpb = p.block / BK;  // block_size is a multiple of BK (checked on the host)
       qb0 = t0 / p.block;
       qb1 = t1 / p.block;
+      tpb_shift = __builtin_ctz((unsigned)tpb);
+      blk_shift = __builtin_ctz((unsigned)p.block);
+      if (p.stride_blocks > 0 && (p.stride_blocks & (p.stride_blocks - 1)) == 0) stride_mask = p.stride_blocks - 1;
     }
   }
 
@@ -214,7 +223,8 @@ struct KeyTilesT {
     if (kb < p.sink_blocks || kb >= qb0 - p.local_blocks) return kb;
     int c = qb0 - p.local_blocks;
     if (p.stride_blocks > 0) {
-      const int m = ((kb + p.stride_blocks - 1) / p.stride_blocks) * p.stride_blocks;
+      const int m = stride_mask >= 0 ? (kb + stride_mask) & ~stride_mask
+                                     : ((kb + p.stride_blocks - 1) / p.stride_blocks) * p.stride_blocks;
       if (m < c) c = m;
     }
     return c;
@@ -227,9 +237,9 @@ struct KeyTilesT {
     if (mode() == MODE_STREAM) {
       if (kt >= sink_end && kt < win_begin) kt = win_begin;
     } else if (mode() == MODE_BLOCK) {
-      const int kb = kt / tpb;
+      const int kb = kt >> tpb_shift;
       const int nb = next_block(kb);
-      if (nb != kb) kt = nb * tpb;
+      if (nb != kb) kt = nb << tpb_shift;
     }
     return kt <= last ? kt : -1;
   }
@@ -241,9 +251,10 @@ struct KeyTilesT {
     if (k1 >= k_end) return true;  // keys past the end of the range (or of the sequence)
     if (mode() == MODE_FULL) return false;
     if (mode() == MODE_STREAM) return !(k1 < p.sink || k0 > t1 - p.window);
-    const int kb = k0 / p.block;
-    return !(kb < p.sink_blocks || kb >= qb1 - p.local_blocks ||
-             (p.stride_blocks > 0 && kb % p.stride_blocks == 0));
+    const int kb = k0 >> blk_shift;
+    const bool on_stride = p.stride_blocks > 0 &&
+                           (stride_mask >= 0 ? (kb & stride_mask) == 0 : kb % p.stride_blocks == 0);
+    return !(kb < p.sink_blocks || kb >= qb1 - p.local_blocks || on_stride);
   }
 
   // Visited tiles in [0, x] for x <= diag, ignoring the key range, without enumeration.
