@@ -40,11 +40,11 @@ constexpr int LIST_MAX_QB = 8;  // query blocks one item may span
 // Key tiles of one block-list item, read from the LDS visibility words vis[kb - kb0].  Same
 // interface as KeyTilesT; every call is made by the whole workgroup with uniform arguments.
 struct ListTiles {
-  int BK, tpb, t0, t1, lo, last, k_end, qb0, kb0, kb_last;
+  int BK, tpb, tpb_shift, t0, t1, lo, last, k_end, qb0, kb0, kb_last;  // tpb = 1 << tpb_shift
   unsigned full_mask;  // every query block of the item
   const uint32_t* vis;
 
-  __device__ unsigned vis_of(int kt) const { return vis[kt / tpb - kb0]; }
+  __device__ unsigned vis_of(int kt) const { return vis[(kt >> tpb_shift) - kb0]; }
 
   // Does the list of query block qblk (absolute) hold the key block of tile kt?
   __device__ bool lists(int kt, int qblk) const {
@@ -55,14 +55,14 @@ struct ListTiles {
   __device__ int next(int kt) const {
     if (kt < lo) kt = lo;
     if (kt > last) return -1;
-    const int kb = kt / tpb;
+    const int kb = kt >> tpb_shift;
     if (vis[kb - kb0] != 0) return kt;
     const int lane = __lane_id();
     for (int base = kb + 1; base <= kb_last; base += 64) {
       const int b = base + lane;
       const uint64_t m = __ballot(b <= kb_last && vis[b - kb0] != 0);
       if (m != 0) {
-        const int t = (base + __ffsll((unsigned long long)m) - 1) * tpb;
+        const int t = (base + __ffsll((unsigned long long)m) - 1) << tpb_shift;
         return t <= last ? t : -1;
       }
     }
@@ -87,6 +87,7 @@ __device__ inline ListTiles list_tiles(uint32_t* vis, const Pattern& p, int b, i
   ListTiles t;
   t.BK = BK;
   t.tpb = p.block / BK;
+  t.tpb_shift = __builtin_ctz((unsigned)t.tpb);  // block and BK are powers of two
   t.t0 = a0;
   t.t1 = a1;
   t.k_end = k_end;
