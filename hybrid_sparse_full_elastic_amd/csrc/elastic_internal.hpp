@@ -183,7 +183,7 @@ struct KeyTilesT {
   // block: log2 of tiles per block and of the block size (both powers of two), and
   // stride_blocks - 1 when the stride is a power of two (else -1): the per-step tile walk
   // then takes shifts and masks instead of scalar divisions
-  int tpb_shift, blk_shift, stride_mask;
+  int tpb_shift, blk_shift, stride_mask, stride_shift;
 
   __host__ __device__ int mode() const { return M >= 0 ? M : mode_rt; }
 
@@ -199,7 +199,7 @@ struct KeyTilesT {
     win_begin = 0;
     tpb = 1;
     qb0 = qb1 = 0;
-    tpb_shift = blk_shift = 0;
+    tpb_shift = blk_shift = stride_shift = 0;
     stride_mask = -1;
     if (mode() == MODE_STREAM) {
       const int sink_keys = p.sink < t1 + 1 ? p.sink : t1 + 1;
@@ -212,7 +212,10 @@ struct KeyTilesT {
       qb1 = t1 / p.block;
       tpb_shift = __builtin_ctz((unsigned)tpb);
       blk_shift = __builtin_ctz((unsigned)p.block);
-      if (p.stride_blocks > 0 && (p.stride_blocks & (p.stride_blocks - 1)) == 0) stride_mask = p.stride_blocks - 1;
+      if (p.stride_blocks > 0 && (p.stride_blocks & (p.stride_blocks - 1)) == 0) {
+        stride_mask = p.stride_blocks - 1;
+        stride_shift = __builtin_ctz((unsigned)p.stride_blocks);
+      }
     }
   }
 
@@ -271,7 +274,7 @@ struct KeyTilesT {
     // the diagonal block qb1 is visited up to diag
     const int a = p.sink_blocks < qb1 ? p.sink_blocks : qb1;
     const int b0 = qb0 - p.local_blocks > 0 ? qb0 - p.local_blocks : 0;
-    const int xb = x / tpb;
+    const int xb = x >> tpb_shift;
     const int m = xb < qb1 ? xb : qb1;  // whole visible blocks in [0, m)
     int nb;
     if (a >= b0) {
@@ -279,11 +282,14 @@ struct KeyTilesT {
     } else {
       nb = (m < a ? m : a) + (m > b0 ? m - b0 : 0);
       const int top = m < b0 ? m : b0;
-      if (p.stride_blocks > 0 && top > a)
-        nb += (top + p.stride_blocks - 1) / p.stride_blocks - (a + p.stride_blocks - 1) / p.stride_blocks;
+      if (p.stride_blocks > 0 && top > a)  // stride multiples in [a, top) (both >= 0)
+        nb += stride_mask >= 0
+                  ? ((top + stride_mask) >> stride_shift) - ((a + stride_mask) >> stride_shift)
+                  : (top + p.stride_blocks - 1) / p.stride_blocks - (a + p.stride_blocks - 1) / p.stride_blocks;
     }
     if (xb >= qb1) return nb * tpb + (x - qb1 * tpb + 1);
-    const bool vis = xb < a || xb >= b0 || (p.stride_blocks > 0 && xb % p.stride_blocks == 0);
+    const bool vis = xb < a || xb >= b0 ||
+                     (p.stride_blocks > 0 && (stride_mask >= 0 ? (xb & stride_mask) == 0 : xb % p.stride_blocks == 0));
     return nb * tpb + (vis ? x - xb * tpb + 1 : 0);
   }
 

@@ -60,9 +60,12 @@ __device__ inline long long block_scan(long long x, long long* tmp, long long* t
   return r;
 }
 
+// BK (key tile width) is a template argument so that the tile arithmetic of the cost model
+// divides by a constant.
+template <int BK>
 __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     SeqGeom geo, int batch, int n_kv_heads, const int32_t* __restrict__ head_mask, Pattern pat,
-    int BT, int BK, int64_t max_items, int32_t* __restrict__ tile_prefix,
+    int BT, int64_t max_items, int32_t* __restrict__ tile_prefix,
     int32_t* __restrict__ cost_tmp, WorkItem* __restrict__ items, int32_t* __restrict__ sched) {
   __shared__ int hist[SCHED_NX * PLAN_BUCKETS];
   __shared__ long long scan_tmp[PLAN_WAVES];
@@ -171,6 +174,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
   }
   block_scan(wsum, scan_tmp, &total);
   const long long W = total > 0 ? total : 1;
+  const double inv_2w = (double)SCHED_NX / (2.0 * (double)W);
 
   // 3. Cut: lay the groups (sequence, KV head) end to end and give item L of that line to XCD
   //    floor(8 * (weight before L + half its own) / W).  Line index L: sequence b owns
@@ -196,7 +200,9 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     const long long inc = block_scan(w, scan_tmp, &total);
     if (L < nitem) {
       const long long mid2 = 2 * (carry + inc - w) + w;  // twice the item's midpoint
-      const int x = (int)min((long long)SCHED_NX - 1, mid2 * SCHED_NX / (2 * W));
+      // floor(8 * midpoint / W) in fp64 (a 64-bit integer division costs far more; a boundary
+      // rounded the other way only moves one item to the neighbouring queue)
+      const int x = (int)min((double)(SCHED_NX - 1), floor((double)mid2 * inv_2w));
       cost[u] = c | (x << 28);
       atomicAdd(&hist[x * PLAN_BUCKETS + (PLAN_BUCKETS - 1 - bucket_of(c))], 1);
     }
@@ -250,8 +256,14 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
 hipError_t launch_plan(const SeqGeom& geo, int batch, int n_kv_heads, const int32_t* head_mask,
                        const Pattern& pat, int BT, int BK, int64_t max_items, int32_t* tile_prefix,
                        int32_t* cost_tmp, WorkItem* items, int32_t* sched, hipStream_t stream) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, geo, batch, n_kv_heads,
-                     head_mask, pat, BT, BK, max_items, tile_prefix, cost_tmp, items, sched);
+  if (BK == BF16_BK)
+    hipLaunchKernelGGL(plan_kernel<BF16_BK>, dim3(1), dim3(PLAN_THREADS), 0, stream, geo, batch,
+                       n_kv_heads, head_mask, pat, BT, max_items, tile_prefix, cost_tmp, items, sched);
+  else if (BK == F32_BK)
+    hipLaunchKernelGGL(plan_kernel<F32_BK>, dim3(1), dim3(PLAN_THREADS), 0, stream, geo, batch,
+                       n_kv_heads, head_mask, pat, BT, max_items, tile_prefix, cost_tmp, items, sched);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
