@@ -183,28 +183,42 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
   //    stretch of the line -- a queue -- holds long and short items alike (causal costs grow
   //    with the query tile) and every queue ends on short items.  The XCD goes into the top
   //    bits of cost[u].
+  //    Each thread takes CUT_PT consecutive line positions per round, so a round needs one
+  //    block-wide scan.
+  constexpr int CUT_PT = 4;
   carry = 0;
-  for (int base = 0; base < nitem; base += PLAN_THREADS) {
-    const int L = base + tid;
-    int u = -1, c = 0;
-    if (L < nitem) {
-      const int b = seq_of_tile(L / n_kv_heads);
-      const int p0 = prefix_of(b), nt = prefix_of(b + 1) - p0;
-      const int r = L - p0 * n_kv_heads;
-      const int g = r / nt, j = r - g * nt;
-      const int qt = (j & 1) ? nt - 1 - (j >> 1) : (j >> 1);  // 0, nt-1, 1, nt-2, ...
-      u = (p0 + qt) * n_kv_heads + g;
-      c = cost[u];
+  for (int base = 0; base < nitem; base += PLAN_THREADS * CUT_PT) {
+    int uu[CUT_PT], cc[CUT_PT];
+    long long wt = 0;  // this thread's weight in the round
+#pragma unroll
+    for (int r = 0; r < CUT_PT; ++r) {
+      const int L = base + tid * CUT_PT + r;
+      uu[r] = -1;
+      cc[r] = 0;
+      if (L < nitem) {
+        const int b = seq_of_tile(L / n_kv_heads);
+        const int p0 = prefix_of(b), nt = prefix_of(b + 1) - p0;
+        const int rr = L - p0 * n_kv_heads;
+        const int g = rr / nt, j = rr - g * nt;
+        const int qt = (j & 1) ? nt - 1 - (j >> 1) : (j >> 1);  // 0, nt-1, 1, nt-2, ...
+        uu[r] = (p0 + qt) * n_kv_heads + g;
+        cc[r] = cost[uu[r]];
+        wt += cc[r] + ITEM_OVERHEAD;
+      }
     }
-    const long long w = L < nitem ? c + ITEM_OVERHEAD : 0;
-    const long long inc = block_scan(w, scan_tmp, &total);
-    if (L < nitem) {
-      const long long mid2 = 2 * (carry + inc - w) + w;  // twice the item's midpoint
+    const long long inc = block_scan(wt, scan_tmp, &total);
+    long long before = carry + inc - wt;  // line weight before this thread's first position
+#pragma unroll
+    for (int r = 0; r < CUT_PT; ++r) {
+      if (uu[r] < 0) continue;
+      const long long w = cc[r] + ITEM_OVERHEAD;
+      const long long mid2 = 2 * before + w;  // twice the item's midpoint
+      before += w;
       // floor(8 * midpoint / W) in fp64 (a 64-bit integer division costs far more; a boundary
       // rounded the other way only moves one item to the neighbouring queue)
       const int x = (int)min((double)(SCHED_NX - 1), floor((double)mid2 * inv_2w));
-      cost[u] = c | (x << 28);
-      atomicAdd(&hist[x * PLAN_BUCKETS + (PLAN_BUCKETS - 1 - bucket_of(c))], 1);
+      cost[uu[r]] = cc[r] | (x << 28);
+      atomicAdd(&hist[x * PLAN_BUCKETS + (PLAN_BUCKETS - 1 - bucket_of(cc[r]))], 1);
     }
     carry += total;
   }
