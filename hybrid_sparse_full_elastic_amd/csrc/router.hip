@@ -10,7 +10,7 @@
 // Pooling streams hidden[T, d] once from HBM and dominates the router's time, so it is
 // written for bandwidth: many workgroups, each summing a slab of up to ROUTE_SLAB rows of a
 // 512-column strip with 16-byte loads (4 waves interleave rows, 4 rows in flight per lane).
-// A second kernel finishes the mean, the MLP and the threshold.  No floating-point atomics
+// Two small kernels finish the mean, the MLP and the threshold.  No floating-point atomics
 // anywhere: every sum runs in a fixed order, so results are bitwise reproducible.
 #include "elastic_internal.hpp"
 
@@ -69,12 +69,9 @@ __device__ inline void load8(const void* hidden, int dtype, int64_t off, float* 
 // Partial column sums of one slab: partials[slab, col].
 __global__ __launch_bounds__(RT) void route_pool_partial(
     const void* __restrict__ hidden, int dtype, const int32_t* __restrict__ cu, int batch,
-    int64_t total, int d, int pool_head, int pool_tail, int slab_rows, float* __restrict__ partials,
-    int32_t* __restrict__ counters) {
+    int64_t total, int d, int pool_head, int pool_tail, int slab_rows, float* __restrict__ partials) {
   __shared__ float red[3][64][8 + 1];
   const int slab = blockIdx.x;
-  if (slab == 0 && blockIdx.y == 0)  // completion counters of route_head start at zero
-    for (int b = threadIdx.x; b < batch; b += RT) counters[b] = 0;
   int b = -1, slab_in = 0, acc = 0;
   SeqPool s{};
   for (int bb = 0; bb < batch; ++bb) {
@@ -127,24 +124,23 @@ __global__ __launch_bounds__(RT) void route_pool_partial(
   }
 }
 
-// route_head: workgroup (b, ch) finishes the mean of sequence b over HCOLS columns (the
-// sequence's slab partials summed in slab order), multiplies that strip into every row of W1
-// (partial z), and the last workgroup of the sequence to finish sums the partial z in strip
-// order, applies ReLU and W2 and thresholds the logits.  Completion is counted with one
-// integer atomic per sequence; all floating-point sums run in a fixed order.
+// route_strip: workgroup (b, ch) finishes the mean of sequence b over HCOLS columns (the
+// sequence's slab partials summed in slab order) and multiplies that strip into every row of
+// W1 (partial z).  route_finish (one workgroup per sequence) sums the partial z in strip order,
+// applies ReLU and W2 and thresholds the logits.  The kernel boundary makes the partial z
+// visible: a completion counter inside one kernel needs a device-scope fence per workgroup,
+// which writes back the L2 and measured about 17 us.  All floating-point sums run in a fixed
+// order.
 constexpr int HCOLS = ROUTE_HCOLS;
 constexpr int HT = 1024;          // threads of route_head: 16 waves split a sequence's slabs
 constexpr int HW = HT / 64;
 
-__global__ __launch_bounds__(HT) void route_head(
+__global__ __launch_bounds__(HT) void route_strip(
     const float* __restrict__ partials, const int32_t* __restrict__ cu, int batch, int64_t total,
     int d, int pool_head, int pool_tail, int slab_rows, const float* __restrict__ w1, int d_router,
-    const float* __restrict__ w2, int n_kv_heads, float threshold, float* __restrict__ zpart,
-    int32_t* __restrict__ counters, float* __restrict__ logits, int32_t* __restrict__ mask) {
+    float* __restrict__ zpart) {
   __shared__ float red[HW][HCOLS];
   __shared__ float hbar[HCOLS];
-  __shared__ float zs[ROUTE_MAX_DR];
-  __shared__ int is_last;
   const int b = blockIdx.x, ch = blockIdx.y, nch = gridDim.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int first = 0;
@@ -205,28 +201,29 @@ __global__ __launch_bounds__(HT) void route_head(
     acc += __shfl_xor(acc, 2);
     if (jrow < d_router && q4 == 0) zpart[((int64_t)b * nch + ch) * ROUTE_MAX_DR + jrow] = acc;
   }
+}
 
-  // 3. the last strip of sequence b finishes: z = sum of strips, logits = W2 relu(z)
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) is_last = atomicAdd(&counters[b], 1) == nch - 1;
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  // z[j]: 4 threads per row each sum a quarter of the strips in order, then the quarters
+constexpr int FT = 256;  // threads of route_finish
+
+__global__ __launch_bounds__(FT) void route_finish(const float* __restrict__ zpart, int nch,
+                                                   int d_router, const float* __restrict__ w2,
+                                                   int n_kv_heads, float threshold,
+                                                   float* __restrict__ logits,
+                                                   int32_t* __restrict__ mask) {
   __shared__ float zq[4][ROUTE_MAX_DR];
+  __shared__ float zs[ROUTE_MAX_DR];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  // z[j]: 4 threads per row each sum a quarter of the strips in order, then the quarters
   {
     const int q4 = tid & 3, per = (nch + 3) / 4;
-    for (int j = tid / 4; j < d_router; j += HT / 4) {
+    for (int j = tid / 4; j < d_router; j += FT / 4) {
       float z = 0.f;
       const int c1 = min(nch, (q4 + 1) * per);
       for (int cs0 = q4 * per; cs0 < c1; cs0 += 16) {
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          x[r] = cs0 + r < c1 ? __hip_atomic_load(&zpart[((int64_t)b * nch + cs0 + r) * ROUTE_MAX_DR + j],
-                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                              : 0.f;
+          x[r] = cs0 + r < c1 ? zpart[((int64_t)b * nch + cs0 + r) * ROUTE_MAX_DR + j] : 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) z += x[r];
       }
@@ -234,9 +231,9 @@ __global__ __launch_bounds__(HT) void route_head(
     }
   }
   __syncthreads();
-  for (int j = tid; j < d_router; j += HT) zs[j] = fmaxf(((zq[0][j] + zq[1][j]) + zq[2][j]) + zq[3][j], 0.f);
+  for (int j = tid; j < d_router; j += FT) zs[j] = fmaxf(((zq[0][j] + zq[1][j]) + zq[2][j]) + zq[3][j], 0.f);
   __syncthreads();
-  for (int gh = tid; gh < n_kv_heads; gh += HT) {
+  for (int gh = tid; gh < n_kv_heads; gh += FT) {
     const float* wg = w2 + (int64_t)gh * d_router;
     float acc = 0.f;
     for (int r = 0; r < d_router; ++r) acc = fmaf(wg[r], zs[r], acc);
@@ -251,7 +248,7 @@ hipError_t launch_route(const void* hidden, int hidden_dtype, const int32_t* cu_
                         int64_t total_tokens, int d_model, int pool_head, int pool_tail,
                         const float* w1, int d_router, const float* w2, int n_kv_heads,
                         float threshold, float* logits_out, int32_t* mask_out, float* partials,
-                        int64_t max_slabs, float* zpart, int32_t* counters, hipStream_t stream) {
+                        int64_t max_slabs, float* zpart, hipStream_t stream) {
   const int chunks = (d_model + RCOLS - 1) / RCOLS;
   // Boundary pooling reads at most pool_head + pool_tail rows per sequence.  Few rows give
   // few slabs, and a 128-row slab is eight dependent load rounds for its workgroup, so such
@@ -269,16 +266,18 @@ hipError_t launch_route(const void* hidden, int hidden_dtype, const int32_t* cu_
       if ((int64_t)batch * per < max_slabs) max_slabs = (int64_t)batch * per;
     }
   }
-  // at least one workgroup: block (0, 0) also clears the completion counters
   hipLaunchKernelGGL(route_pool_partial, dim3((unsigned)(max_slabs > 0 ? max_slabs : 1), chunks),
                      dim3(RT), 0, stream, hidden, hidden_dtype, cu_seqlens, batch, total_tokens,
-                     d_model, pool_head, pool_tail, slab_rows, partials, counters);
+                     d_model, pool_head, pool_tail, slab_rows, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(route_head, dim3(batch, (d_model + HCOLS - 1) / HCOLS), dim3(HT), 0, stream,
-                     partials, cu_seqlens, batch, total_tokens, d_model, pool_head, pool_tail,
-                     slab_rows, w1, d_router, w2, n_kv_heads, threshold, zpart, counters, logits_out,
-                     mask_out);
+  const int nch = (d_model + HCOLS - 1) / HCOLS;
+  hipLaunchKernelGGL(route_strip, dim3(batch, nch), dim3(HT), 0, stream, partials, cu_seqlens, batch,
+                     total_tokens, d_model, pool_head, pool_tail, slab_rows, w1, d_router, zpart);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(route_finish, dim3(batch), dim3(FT), 0, stream, zpart, nch, d_router, w2,
+                     n_kv_heads, threshold, logits_out, mask_out);
   return hipGetLastError();
 }
 
