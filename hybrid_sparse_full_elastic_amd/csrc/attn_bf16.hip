@@ -26,22 +26,28 @@
 //    sums with room to spare, and the result is exact in exact arithmetic for any m.
 //  * Masks are evaluated only on tiles that cross a causal, sink, window or block boundary,
 //    and tiles no query of the item may see are never loaded (streaming items cost
-//    O(sink + window), not O(n)).  Each item runs a loop compiled for its mode.
-//  * K/V tiles travel global -> LDS by buffer_load ... lds (no register staging) into three
-//    LDS slots each: K three tiles ahead, V two tiles ahead, so a load has two tile steps to
-//    land.  Rows past the sequence end read as zero through the buffer descriptor's range.
-//    Tiles are unpadded with XOR swizzles of the 16-byte chunks chosen so the K row reads
-//    and the transposing V reads are free of LDS bank conflicts.
+//    O(sink + window), not O(n)).  Each item runs a loop compiled for its mode.  A lane turns
+//    its kept keys of an edge tile into two 32-bit words, so an element costs one bit
+//    extract and one select.
+//  * K/V tiles travel global -> LDS by buffer_load ... lds (no register staging): four K
+//    slots (K four tiles ahead) and three V slots (V two tiles ahead), so a load has two tile
+//    steps to land.  Rows past the sequence end read as zero through the buffer descriptor's
+//    range.  Tiles are unpadded with XOR swizzles of the 16-byte chunks chosen so the K row
+//    reads and the transposing V reads are free of LDS bank conflicts.
 //  * Per tile step j, two instruction regions fenced with sched_barrier so the issue order is
 //    the written one: the Q.K^T MFMAs of tile j+1 with the exp2 / bf16 packing / row sums of
-//    tile j between them (K fragments read five MFMAs ahead), then the P.V MFMAs of tile j
-//    with the transposing V reads (four ahead) between them.  A
-//    wave keeps its MFMA pipe fed while its own softmax work issues beside it, and the two
+//    tile j between them (K fragments read five MFMAs ahead, the step's DMA issued halfway,
+//    the first V fragments read during the last MFMAs), then the P.V MFMAs of tile j with
+//    the transposing V reads (four ahead) between them and, after them, the first K
+//    fragments of tile j+2 (it landed one barrier early), so the next step starts on MFMAs.
+//    A wave keeps its MFMA pipe fed while its own softmax work issues beside it, and the two
 //    waves sharing a SIMD fill each other's gaps.  The mask of an edge tile sits between the
 //    regions; one barrier per step.
-//  * Epilogue: each wave stages its 32 normalised rows in the idle tile slots (same swizzle)
-//    and writes whole O rows with 16-byte stores, so the G heads of a token leave as one
-//    contiguous run instead of scattered 8-byte pieces.
+//  * Persistent grid: each workgroup claims items from its XCD's queue; the next item is
+//    claimed in the current item's prologue and its descriptor copied to LDS meanwhile.
+//  * Epilogue: each wave stages its 32 normalised rows in the idle tile slots (same swizzle) and
+//    writes whole O rows with 16-byte non-temporal stores, so the G heads of a token leave as
+//    one contiguous run instead of scattered 8-byte pieces.
 #include <type_traits>
 
 #include "elastic_internal.hpp"
@@ -578,9 +584,9 @@ __device__ __forceinline__ void attn_item(
     }
   }
 
-  // ---- epilogue (O is written once: non-temporal stores, 1-2% faster on sparse heads):
-  // normalise, stage the wave's 32 rows in LDS (every wave passed the last
-  // barrier, so the K/V slots are idle), then write whole O rows with 16-byte stores
+  // ---- epilogue: normalise, stage the wave's 32 rows in LDS (every wave passed the last
+  // barrier, so the tile slots are idle), then write whole O rows with 16-byte stores (O is
+  // written once: non-temporal stores, 1-2% faster on sparse heads)
   const float lt = half_sum(l_run);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   uint16_t* stage = reinterpret_cast<uint16_t*>(&lds) + wave * 32 * D;  // 32 rows x D, swizzled
