@@ -415,9 +415,11 @@ __device__ __forceinline__ void attn_item(
     // the scalar work of a step shrinks to the DMA descriptors and one loop test.  Used for
     // full items, whose tiles below the diagonal form one such run; for the shorter runs of
     // sparse items the extra loop copy costs more than it saves.
-    auto step = [&](auto steady_tag, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    auto step = [&](auto steady_tag, f32x16 (&sc)[2], f32x16 (&sn)[2], auto slot_tag) {
       constexpr bool STEADY = decltype(steady_tag)::value;
-      const int sk1 = (skj + 1) & (NSK - 1), sk2 = (skj + 2) & (NSK - 1);
+      constexpr int SKC = decltype(slot_tag)::value;
+      const int skj_ = SKC >= 0 ? SKC : skj;
+      const int sk1 = (skj_ + 1) & (NSK - 1), sk2 = (skj_ + 2) & (NSK - 1);
       const int sv2 = svj == 0 ? NSV - 1 : svj - 1;
       const int n_dma = STEADY ? 2 * CPT : (kt_n4 >= 0 ? CPT : 0) + (kt_n2 >= 0 ? CPT : 0);
       const bool has_next = STEADY || kt_n1 >= 0;
@@ -471,10 +473,10 @@ __device__ __forceinline__ void attn_item(
           if (i >= NQK - NVPRE) vread(i - (NQK - NVPRE));
           if (i == NQK / 2) {
             if (STEADY) {
-              dma_full(kbase, kt_n4, kslot + skj * SLOT, k_voff);
+              dma_full(kbase, kt_n4, kslot + skj_ * SLOT, k_voff);
               dma_full(vbase, kt_n2, vslot + sv2 * SLOT, v_voff);
             } else {
-              if (kt_n4 >= 0) dma(kbase, kt_n4, kslot + skj * SLOT, k_voff);
+              if (kt_n4 >= 0) dma(kbase, kt_n4, kslot + skj_ * SLOT, k_voff);
               if (kt_n2 >= 0) dma(vbase, kt_n2, vslot + sv2 * SLOT, v_voff);
             }
           }
@@ -560,15 +562,24 @@ __device__ __forceinline__ void attn_item(
       // Full items visit consecutive tiles.  A pair of steady steps from tile j loads tiles up
       // to j+5 (whole inside the key range), advances the schedule to j+6 (a visited tile) and
       // computes S of tiles j+1, j+2 (below the diagonal and the key range's end: no mask).
-      while (tiles.steady_pair(kt_cur)) {
-        step(SteadyT{}, s0, s1);
-        step(SteadyT{}, s1, s0);
+      // Two pairs per iteration keep the K slot indices compile-time constants, so the K
+      // fragment addresses fold into the LDS read offsets (9 fewer VALU per step, -0.7%).
+      using K0 = std::integral_constant<int, 0>;
+      using K1 = std::integral_constant<int, 1>;
+      using K2 = std::integral_constant<int, 2>;
+      using K3 = std::integral_constant<int, 3>;
+      // the steady loop starts right after the prologue (K slot 0) and keeps the slot period
+      while (tiles.steady_pair(kt_cur) && tiles.steady_pair(kt_cur + 2)) {
+        step(SteadyT{}, s0, s1, K0{});
+        step(SteadyT{}, s1, s0, K1{});
+        step(SteadyT{}, s0, s1, K2{});
+        step(SteadyT{}, s1, s0, K3{});
       }
     }
     while (true) {
-      step(GeneralT{}, s0, s1);
+      step(GeneralT{}, s0, s1, std::integral_constant<int, -1>{});
       if (kt_cur < 0) break;
-      step(GeneralT{}, s1, s0);
+      step(GeneralT{}, s1, s0, std::integral_constant<int, -1>{});
       if (kt_cur < 0) break;
     }
   }
