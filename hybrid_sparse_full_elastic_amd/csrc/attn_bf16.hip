@@ -467,7 +467,15 @@ __device__ __forceinline__ void attn_item(
             const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
             pop[kb][e >> 3][e & 7] = pp[0];
             pop[kb][e >> 3][(e & 7) + 1] = pp[1];
-            ls[pair & 3] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls[pair & 3], false);
+            if (pair < 4) {
+              // the first pair of each row-sum chain: the three-operand form with an inline
+              // zero addend (the accumulating form needs a v_mov of zero first)
+              float r0;
+              asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r0) : "v"(__builtin_bit_cast(uint32_t, pp)), "s"(0x3f803f80u));
+              ls[pair & 3] = r0;
+            } else {
+              ls[pair & 3] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls[pair & 3], false);
+            }
           }
           // the first V fragments of region 2, during the last MFMAs
           if (i >= NQK - NVPRE) vread(i - (NQK - NVPRE));
