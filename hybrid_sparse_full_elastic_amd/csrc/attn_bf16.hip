@@ -195,6 +195,7 @@ __device__ __forceinline__ void attn_item(
   const int blk_shift = 31 - __clz(pat.block);  // block sizes are powers of two
 
   const int lane = tid & 63, wave = tid >> 6;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // uniform: LDS DMA bases in scalar registers
   const int l32 = lane & 31, half = lane >> 5;
   const int64_t kv_row = (int64_t)Hkv * D;  // elements between consecutive tokens of k / v
   const uint16_t* kbase = k + sp.k0 * kv_row + (int64_t)g * D;
@@ -237,14 +238,14 @@ __device__ __forceinline__ void attn_item(
         BK * (int)kv_row * 2, 0x00020000);
 #pragma unroll
     for (int m = 0; m < CPT; ++m)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(slot + (wave * CPT + m) * 512), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(slot + (wave_s * CPT + m) * 512), 16,
                                                voff[m], 0, 0, 0);
   };
   auto dma = [&](const uint16_t* base, int kt, uint16_t* slot, const int (&voff)[CPT]) {
     const auto rs = tile_rsrc(base, kt);
 #pragma unroll
     for (int m = 0; m < CPT; ++m)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(slot + (wave * CPT + m) * 512), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(slot + (wave_s * CPT + m) * 512), 16,
                                                voff[m], 0, 0, 0);
   };
 
