@@ -91,9 +91,8 @@ __device__ inline float max3f(float a, float b, float c) {
 
 // An empty statement that takes the values in registers: the computations producing them stay
 // above it.
-__device__ __forceinline__ void keep_here(const bf16x8 (&p)[2][2], const float (&l)[4]) {
-  asm volatile("" ::"v"(p[0][0]), "v"(p[0][1]), "v"(p[1][0]), "v"(p[1][1]), "v"(l[0]), "v"(l[1]),
-               "v"(l[2]), "v"(l[3]));
+__device__ __forceinline__ void keep_here(const bf16x8 (&p)[2][2], const float l) {
+  asm volatile("" ::"v"(p[0][0]), "v"(p[0][1]), "v"(p[1][0]), "v"(p[1][1]), "v"(l));
 }
 __device__ __forceinline__ void lds_wait_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -432,7 +431,9 @@ __device__ __forceinline__ void attn_item(
       constexpr int PPM = 16 / NQK;  // weight pairs per Q.K^T MFMA
       constexpr int AHEAD = 5;
       bf16x8 pop[2][2];
-      float ls[4] = {0.f, 0.f, 0.f, 0.f};
+      // row sum of the tile's weights: one dependent chain (the dot2 steps sit one per
+      // MFMA, far enough apart to hide their latency; no combining adds)
+      float ls = 0.f;
       // transposing reads of V_j (landed before the last barrier)
       const uint16_t* vs = vslot + svj * SLOT;
       bf16x8 av[NPV];
@@ -468,14 +469,14 @@ __device__ __forceinline__ void attn_item(
             const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
             pop[kb][e >> 3][e & 7] = pp[0];
             pop[kb][e >> 3][(e & 7) + 1] = pp[1];
-            if (pair < 4) {
-              // the first pair of each row-sum chain: the three-operand form with an inline
-              // zero addend (the accumulating form needs a v_mov of zero first)
+            if (pair == 0) {
+              // the first pair of the row sum: the three-operand form with an inline zero
+              // addend (the accumulating form needs a v_mov of zero first)
               float r0;
               asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r0) : "v"(__builtin_bit_cast(uint32_t, pp)), "s"(0x3f803f80u));
-              ls[pair & 3] = r0;
+              ls = r0;
             } else {
-              ls[pair & 3] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls[pair & 3], false);
+              ls = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls, false);
             }
           }
           // the first V fragments of region 2, during the last MFMAs
@@ -497,7 +498,7 @@ __device__ __forceinline__ void attn_item(
       // The weights of tile j used the running maximum m.  A row whose partial sum passes
       // 2^70 (some weight above 2^64: the first tiles of a row, or a sharp rise of its scores)
       // is redone with the tile's own maximum; inf and NaN sums take the same path.
-      if (__builtin_amdgcn_ballot_w64(!((ls[0] + ls[1]) + (ls[2] + ls[3]) <= 0x1p70f)) != 0) {
+      if (__builtin_amdgcn_ballot_w64(!(ls <= 0x1p70f)) != 0) {
         float m0 = max3f(sc[0][0], sc[1][0], sc[0][1]);
         float m1 = max3f(sc[1][1], sc[0][2], sc[1][2]);
 #pragma unroll
@@ -516,8 +517,7 @@ __device__ __forceinline__ void attn_item(
           for (int e = 0; e < 16; ++e) oacc[db][e] *= al;
         const float nm = -m_sc;
         const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ls[r] = 0.f;
+        ls = 0.f;
 #pragma unroll
         for (int pair = 0; pair < 16; ++pair) {
           const int kb = pair >> 3, e = (pair & 7) * 2;
@@ -526,7 +526,7 @@ __device__ __forceinline__ void attn_item(
           const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
           pop[kb][e >> 3][e & 7] = pp[0];
           pop[kb][e >> 3][(e & 7) + 1] = pp[1];
-          ls[pair & 3] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls[pair & 3], false);
+          ls = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls, false);
         }
       }
       if (!STEADY && has_next && tiles.needs_mask(kt_n1)) apply_mask(sn, kt_n1);
@@ -546,7 +546,7 @@ __device__ __forceinline__ void attn_item(
                 *reinterpret_cast<const bf16x8*>(kn + ((i - (NPV - NPRE)) & 1) * 32 * D + k_roff[(i - (NPV - NPRE)) >> 1]);
           __builtin_amdgcn_sched_barrier(0);
         }
-        l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        l_run += ls;
       }
       const int kt_n5 = STEADY ? kt_n4 + 1 : (kt_n4 >= 0 ? tiles.next(kt_n4 + 1) : -1);
       // this step's DMA may stay in flight; the previous step's (K_{j+3}, V_{j+1}) must land
