@@ -214,6 +214,30 @@ def test_router_boundary_pooling_and_empty_sequence():
         assert np.all(lg[1] == 0) and np.all(mask.cpu().numpy()[1] == 0)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_router_ragged_strips_wide_mlp(dtype):
+    """d_model not a multiple of the 64-column strip (last strip partial), a router width of 200
+    (several passes of the finishing kernel), 12 KV heads, a varlen batch; repeated calls agree
+    bit for bit."""
+    lens = [777, 64, 1, 2050]
+    T, d, dr, hkv = sum(lens), 1000, 200, 12
+    hidden = syn.draw_bf16_bits(31, 3, (T, d))
+    if dtype == "fp32":
+        hidden = (hidden.astype(np.uint32) << 16).view(np.float32)
+    w1 = syn.draw_f32(31, 4, (dr, d), 0.1)
+    w2 = syn.draw_f32(31, 5, (hkv, dr), 0.1)
+    cu_np = np.cumsum([0] + lens).astype(np.int32)
+    cu = torch.tensor(cu_np, device=H.DEV)
+    logits, mask = ext.route(H.to_dev(hidden), H.to_dev(w1), H.to_dev(w2), cu_seqlens=cu)
+    ref = oracle.route(hidden, cu_np, w1, w2, 0.0)
+    lg = logits.cpu().numpy()
+    np.testing.assert_allclose(lg, ref["logits"], rtol=1e-4, atol=1e-6)
+    outside = np.abs(ref["logits"]) >= 1e-5
+    np.testing.assert_array_equal(mask.cpu().numpy()[outside], ref["mask"][outside])
+    logits2, _ = ext.route(H.to_dev(hidden), H.to_dev(w1), H.to_dev(w2), cu_seqlens=cu)
+    np.testing.assert_array_equal(lg, logits2.cpu().numpy())
+
+
 @pytest.mark.parametrize("frac", [0.0, 0.25, 0.5, 0.75, 1.0])
 def test_qwen_64k_sparse_fraction_sweep(frac):
     w = syn.WORKLOADS["qwen-64k-stream-sweep"]
