@@ -45,7 +45,7 @@ What is computed (readings of points the summary leaves open are marked READING)
                      lse = log(e^a + e^b),  o = e^(a - lse) o_a + e^(b - lse) o_b.
     chunked_prefill  each query chunk attends every key up to its own end (the queries
                      are the last positions of the keys), chunk results concatenated.
-    block lists      READING (the survey's per-head block lists, the consumer half of
+    block lists      READING (explicit per-head block lists, the consumer half of
                      content-based block selection): the key blocks query block qb of KV head
                      g in sequence b may see are given explicitly, key blocks after qb are
                      ignored (causal), and a query sees key j iff j <= i and j's block is
