@@ -136,7 +136,7 @@ __global__ __launch_bounds__(RT) void route_pool_partial(
 // which writes back the L2 and measured about 17 us.  All floating-point sums run in a fixed
 // order.
 constexpr int HCOLS = ROUTE_HCOLS;
-constexpr int HT = 1024;          // threads of route_head: 16 waves split a sequence's slabs
+constexpr int HT = 1024;          // threads of route_strip: 16 waves split a sequence's slabs
 constexpr int HW = HT / 64;
 
 __global__ __launch_bounds__(HT) void route_strip(
