@@ -57,6 +57,51 @@ def _run(cmd, verbose):
         print(err, file=sys.stderr)
 
 
+def _llvm_tool(name: str) -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    path = os.path.join(rocm, "llvm", "bin", name)
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not found; the ROCm LLVM tools are required to build libelastic")
+    return path
+
+
+def kernel_metadata(obj: str) -> list:
+    """The AMDGPU metadata (amdhsa.kernels) of the gfx950 code object inside a host object
+    built by this script: its .hip_fatbin section is a clang offload bundle."""
+    import tempfile
+    import yaml
+    with tempfile.TemporaryDirectory() as tmp:
+        fat, co = os.path.join(tmp, "fatbin"), os.path.join(tmp, "device.co")
+        _run([_llvm_tool("llvm-objcopy"), "-O", "binary", "--only-section=.hip_fatbin", obj, fat], False)
+        _run([_llvm_tool("clang-offload-bundler"), "--type=o", "--unbundle", f"--input={fat}",
+              f"--output={co}", f"--targets=hipv4-amdgcn-amd-amdhsa--{ARCH}"], False)
+        r = subprocess.run([_llvm_tool("llvm-readelf"), "--notes", co], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"llvm-readelf failed on {obj}: {r.stderr}")
+    text = r.stdout
+    begin = text.index("---")
+    end = text.index("\n...", begin)
+    return yaml.safe_load(text[begin:end])["amdhsa.kernels"]
+
+
+def check_attn_kernargs(meta: list) -> int:
+    """The bf16 attention kernels read their arguments through the kernel argument segment
+    pointer, as a struct at offset 0.  Every instance must take exactly one explicit argument,
+    by value, at offset 0.  Returns the number of instances checked; raises otherwise."""
+    n = 0
+    for k in meta:
+        if "attn_bf16_kernel" not in k[".name"]:
+            continue
+        explicit = [a for a in k.get(".args", []) if not a[".value_kind"].startswith("hidden_")]
+        if len(explicit) != 1 or explicit[0][".offset"] != 0 or explicit[0][".value_kind"] != "by_value":
+            raise RuntimeError(f"{k['.name']}: kernel arguments {explicit} are not one by-value "
+                               "struct at offset 0, which the kernel's argument reads assume")
+        n += 1
+    if n == 0:
+        raise RuntimeError("no attn_bf16_kernel instance found in the code object")
+    return n
+
+
 def build(verbose: bool = False, jobs: int = 8) -> str:
     """Compile every HIP source for gfx950 and link libelastic.so. Returns the library path."""
     cc = hipcc()
@@ -66,6 +111,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     with ThreadPoolExecutor(max(1, min(jobs, len(srcs)))) as ex:
         list(ex.map(lambda so: _run([cc, *HIPCC_FLAGS, "-c", so[0], "-o", so[1]], verbose),
                     zip(srcs, objs)))
+    check_attn_kernargs(kernel_metadata(os.path.join(BUILD_DIR, "attn_bf16.o")))
     tmp = LIB_PATH + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB_PATH)

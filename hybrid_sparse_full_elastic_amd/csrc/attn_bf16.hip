@@ -676,8 +676,10 @@ __global__ __launch_bounds__(BF16_NW * 64, 1) void attn_bf16_kernel(AttnArgs arg
   // argument segment, where the only explicit argument sits at offset 0: values derived from
   // them are then computed inside the item instead of being held in registers across the
   // whole loop (which spills).  (Taking the address of `args` would copy it to scratch.)
+  // The library build reads every instance's code-object metadata and stops unless `args` is
+  // its one explicit argument, by value at offset 0 of the segment.
   ConstArgs* const base = (ConstArgs*)__builtin_amdgcn_kernarg_segment_ptr();
-  if (base->sched != args.sched || base->items != args.items) return;  // layout as assumed
+  (void)args;
   if (threadIdx.x == 0) {  // the first claim; later ones come from each item's prologue
     const int x = (int)(blockIdx.x % SCHED_NX);
     shm.claim.q0 = base->sched[1 + x];

@@ -6,6 +6,7 @@
 
 #include <math.h>
 #include <mutex>
+#include <vector>
 
 #include "elastic_internal.hpp"
 
@@ -54,6 +55,9 @@ int hip_fail(hipError_t e, const char* where) {
 
 constexpr size_t ALIGN = 256;
 inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+// The kernels move tensor rows with 16-byte loads, stores and LDS copies.
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // ---------------------------------------------------------------- attention sizing
 int attn_rows_per_item(int32_t dtype) { return dtype == ELASTIC_BF16 ? BF16_ROWS : F32_ROWS; }
@@ -214,6 +218,7 @@ int elastic_route(const void* hidden, int32_t hidden_dtype, const int32_t* cu_se
   if (hidden_dtype != ELASTIC_BF16 && hidden_dtype != ELASTIC_FP32) return ELASTIC_EUNSUPPORTED;
   if (d_model % 8 != 0 || d_router > ROUTE_MAX_DR || n_kv_heads > ROUTE_MAX_HKV)
     return ELASTIC_EUNSUPPORTED;
+  if (total_tokens > 0 && !aligned16(hidden)) return ELASTIC_EINVAL;
   const RouteWorkspace lay = route_layout(batch, total_tokens, d_model);
   if (workspace == nullptr || workspace_bytes < lay.total) return ELASTIC_EWORKSPACE;
   char* ws = static_cast<char*>(workspace);
@@ -251,6 +256,8 @@ int attn_call(const char* who, const void* q, const void* k, const void* v, void
     return ELASTIC_EINVAL;
   if (total_q > 0 && (q == nullptr || o == nullptr)) return ELASTIC_EINVAL;
   if (total_k > 0 && (k == nullptr || v == nullptr)) return ELASTIC_EINVAL;
+  if (total_q > 0 && !(aligned16(q) && aligned16(o))) return ELASTIC_EINVAL;
+  if (total_k > 0 && !(aligned16(k) && aligned16(v))) return ELASTIC_EINVAL;
   if ((cu_q == nullptr || cu_k == nullptr) && batch != 1) return ELASTIC_EINVAL;
   if (q_pos < -1 || k_pos < 0 || k_pos % 64 != 0) return ELASTIC_EINVAL;
   // absolute positions stay within int32: keys up to k_pos + max_k, queries up to q_pos + max_q
@@ -347,6 +354,7 @@ int elastic_lse_merge(const void* o_a, const float* lse_a, const void* o_b, cons
   if (head_dim != 64 && head_dim != 128) return ELASTIC_EUNSUPPORTED;
   if (rows == 0) return ELASTIC_OK;
   if (!o_a || !lse_a || !o_b || !lse_b || !o_out || !lse_out) return ELASTIC_EINVAL;
+  if (!(aligned16(o_a) && aligned16(o_b) && aligned16(o_out))) return ELASTIC_EINVAL;
   const hipError_t e = launch_lse_merge(dtype, o_a, lse_a, o_b, lse_b, o_out, lse_out, rows,
                                         n_heads, head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "elastic_lse_merge");
@@ -373,7 +381,7 @@ int elastic_retrieval_scores(const void* q, const void* k, int32_t dtype,
   if (head_dim != 64 && head_dim != 128) return ELASTIC_EUNSUPPORTED;
   if (batch == 0) return ELASTIC_OK;
   if (!q || !k || !needle || (!scores_q && !scores_kv)) return ELASTIC_EINVAL;
-  if (((uintptr_t)q | (uintptr_t)k) % 16 != 0) return ELASTIC_EINVAL;
+  if (!(aligned16(q) && aligned16(k))) return ELASTIC_EINVAL;
   if (n_q_heads / n_kv_heads > RET_MAX_G) return ELASTIC_EUNSUPPORTED;
   // grid: chunks x (KV heads x slices of 8 query heads) x sequences
   if (batch > 65535 || (int64_t)n_kv_heads * ((n_q_heads / n_kv_heads + 7) / 8) > 65535)
@@ -423,6 +431,61 @@ int elastic_attn_entries(const int32_t* seqlens_host, int32_t batch,
       int64_t& slot = full ? full_e : sparse_e;
       if (slot < 0) slot = head_entries(seqlens_host[b], full, sparse);
       total += G * slot;
+    }
+  }
+  *entries_out = total;
+  return ELASTIC_OK;
+}
+
+
+int elastic_attn_entries_lists(const int32_t* seqlens_host, int32_t batch,
+                               const int32_t* head_mask_host, int32_t n_q_heads,
+                               int32_t n_kv_heads, int32_t block_size, int32_t list_qblocks,
+                               const int32_t* list_row_ptr_host, const int32_t* list_col_idx_host,
+                               int64_t* entries_out) {
+  if (seqlens_host == nullptr || entries_out == nullptr || batch < 1) return ELASTIC_EINVAL;
+  if (n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads != 0) return ELASTIC_EINVAL;
+  if (list_qblocks < 1 || list_row_ptr_host == nullptr) return ELASTIC_EINVAL;
+  if (block_size != 64 && block_size != 128) return ELASTIC_EUNSUPPORTED;
+  const int64_t rows = (int64_t)batch * n_kv_heads * list_qblocks;
+  if (list_row_ptr_host[0] != 0) return ELASTIC_EINVAL;
+  for (int64_t r = 0; r < rows; ++r)
+    if (list_row_ptr_host[r + 1] < list_row_ptr_host[r]) return ELASTIC_EINVAL;
+  if (list_row_ptr_host[rows] > 0 && list_col_idx_host == nullptr) return ELASTIC_EINVAL;
+  const int64_t G = n_q_heads / n_kv_heads, B = block_size;
+  std::vector<uint8_t> seen((size_t)list_qblocks);
+  int64_t total = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t n = seqlens_host[b];
+    if (n < 0) return ELASTIC_EINVAL;
+    const int64_t nqb = (n + B - 1) / B;
+    if (nqb > list_qblocks) return ELASTIC_EINVAL;  // a query block without a list row
+    for (int32_t g = 0; g < n_kv_heads; ++g) {
+      const bool full = head_mask_host == nullptr || head_mask_host[(int64_t)b * n_kv_heads + g] != 0;
+      if (full) {
+        total += G * (n * (n + 1) / 2);
+        continue;
+      }
+      // query block qb sees its listed earlier blocks whole and its own block causally; blocks
+      // after qb, repeats and negative indices add nothing
+      for (int64_t qb = 0; qb < nqb; ++qb) {
+        const int64_t r = ((int64_t)b * n_kv_heads + g) * list_qblocks + qb;
+        int64_t below = 0;
+        bool diag = false;
+        for (int64_t e = list_row_ptr_host[r]; e < list_row_ptr_host[r + 1]; ++e) {
+          const int64_t kb = list_col_idx_host[e];
+          if (kb < 0 || kb > qb || seen[(size_t)kb]) continue;
+          seen[(size_t)kb] = 1;
+          if (kb == qb) diag = true;
+          else ++below;
+        }
+        for (int64_t e = list_row_ptr_host[r]; e < list_row_ptr_host[r + 1]; ++e) {
+          const int64_t kb = list_col_idx_host[e];
+          if (kb >= 0 && kb <= qb) seen[(size_t)kb] = 0;
+        }
+        const int64_t nr = (qb * B + B < n ? qb * B + B : n) - qb * B;  // query rows of the block
+        total += G * (nr * below * B + (diag ? nr * (nr + 1) / 2 : 0));
+      }
     }
   }
   *entries_out = total;

@@ -28,6 +28,9 @@
  *    elastic_last_error() gives the HIP message (thread-local).
  *  - Concurrent calls are safe when each uses its own workspace; calls that share a
  *    workspace must be ordered on one stream.
+ *  - Tensors the kernels read or write row by row (q, k, v, o, hidden, and the o arrays of
+ *    elastic_lse_merge) must start on a 16-byte boundary: rows move with 16-byte loads,
+ *    stores and LDS copies.  A misaligned pointer returns ELASTIC_EINVAL.
  */
 #ifndef ELASTIC_H_
 #define ELASTIC_H_
@@ -39,7 +42,7 @@
 extern "C" {
 #endif
 
-#define ELASTIC_ABI_VERSION 3
+#define ELASTIC_ABI_VERSION 4
 
 enum elastic_status {
   ELASTIC_OK = 0,
@@ -254,11 +257,32 @@ int elastic_static_assignment(const float* scores, int32_t n_units, double omega
  * 4 * head_dim * entries.  Closed forms: full n(n+1)/2 per head; streaming
  * c(c+1)/2 + (n-c)c with c = min(n, sink+window); block: per query block, the visible
  * earlier blocks times block_size plus the causal diagonal block.  Block lists live on the
- * device: a call with block-list sparse heads returns ELASTIC_EUNSUPPORTED.
+ * device: a call with block-list sparse heads returns ELASTIC_EUNSUPPORTED (count those with
+ * elastic_attn_entries_lists from a host copy of the lists).
  */
 int elastic_attn_entries(const int32_t* seqlens_host, int32_t batch,
                          const int32_t* head_mask_host, int32_t n_q_heads, int32_t n_kv_heads,
                          const elastic_sparse_cfg* sparse, int64_t* entries_out);
+
+/*
+ * Host-only work counter for sparse heads given by explicit block lists (the
+ * ELASTIC_SPARSE_BLOCK_LIST pattern, read from HOST copies of its CSR arrays): allowed score
+ * entries over all query heads.  Full heads count n(n+1)/2 each; for a sparse head, query
+ * block qb counts its listed earlier key blocks whole (block_size keys per query row) and its
+ * own block causally if listed.  Listed blocks after qb, repeated and negative indices count
+ * nothing, as in the kernels.
+ *  seqlens_host       int32 [batch], host
+ *  head_mask_host     int32 [batch, n_kv_heads], host, NULL = all full
+ *  list_row_ptr_host  int32 [batch * n_kv_heads * list_qblocks + 1], host, non-decreasing from 0
+ *  list_col_idx_host  int32 [list_row_ptr_host[last]], host (may be NULL when that is 0)
+ * Errors: ELASTIC_EINVAL (pointers, sizes, a sequence with more query blocks than
+ * list_qblocks, a decreasing row_ptr), ELASTIC_EUNSUPPORTED (block_size not 64 or 128).
+ */
+int elastic_attn_entries_lists(const int32_t* seqlens_host, int32_t batch,
+                               const int32_t* head_mask_host, int32_t n_q_heads,
+                               int32_t n_kv_heads, int32_t block_size, int32_t list_qblocks,
+                               const int32_t* list_row_ptr_host, const int32_t* list_col_idx_host,
+                               int64_t* entries_out);
 
 #ifdef __cplusplus
 }

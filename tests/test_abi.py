@@ -14,7 +14,9 @@ from synth import inputs as syn
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "elastic.h")
 
-ext = pytest.importorskip("hybrid_sparse_full_elastic_amd", reason="libelastic.so not built")
+ext = pytest.importorskip("hybrid_sparse_full_elastic_amd")
+if not os.path.exists(ext.LIB_PATH):
+    pytest.skip("libelastic.so not built", allow_module_level=True)
 L = ext.lib
 FAKE = C.c_void_p(0x1000)  # never dereferenced: validation fails first
 
@@ -192,23 +194,83 @@ def _lists(rows, B=64):
 
 
 def test_block_list_entry_counter_matches_oracle():
-    """The binding's host counter for block lists (the library cannot read device lists)."""
+    """The library's host counter for block lists (elastic_attn_entries_lists, fed host copies
+    of the CSR) against the oracle's enumeration: varlen, mixed head modes, and lists with
+    repeats, blocks after the query block, negative indices and empty rows."""
     rng = np.random.default_rng(5)
-    n, B, hkv = 300, 64, 2
-    nqb = -(-n // B)
+    lens, B, hkv, hq = [300, 0, 64, 129, 1], 64, 2, 8
+    nqb = -(-max(lens) // B)
     rows = []
-    for _ in range(hkv):
+    for _ in range(len(lens) * hkv):
         for qb in range(nqb):
-            rows.append(sorted(set(rng.choice(nqb + 1, size=rng.integers(0, 4)).tolist())))
-    lists = _lists(rows, B)
-    mask = [[0, 1]]
-    assert ext.block_list_entries([n], mask, 8, hkv, lists) == oracle.entries([n], mask, lists, 8, hkv)
-    # the library's counter declines block lists with sparse heads
+            r = rng.integers(-1, nqb + 2, size=rng.integers(0, 6)).tolist()  # repeats, later, -1
+            rows.append(r)
+    lists = dict(_lists(rows, B), qblocks=nqb)
+    for mask in ([[0, 1], [0, 0], [1, 0], [0, 0], [0, 1]], [[0, 0]] * 5, None):
+        got = ext.block_list_entries(lens, mask, hq, hkv, lists)
+        assert got == oracle.entries(lens, mask, lists, hq, hkv), mask
+    with pytest.raises(ValueError):                   # row pointers for too few rows
+        ext.block_list_entries(lens, None, hq, hkv, dict(lists, qblocks=nqb + 1))
+    # the closed-form counter declines block lists with sparse heads
     cfg = ext.SparseCfg(2, 0, 0, 64, 0, 0, 0, nqb, 0x1000, 0x1000)
-    lens = (C.c_int32 * 1)(n)
+    lns = (C.c_int32 * 1)(300)
     m = (C.c_int32 * 2)(0, 1)
     out = C.c_int64(0)
-    assert L.elastic_attn_entries(lens, 1, m, 8, 2, C.byref(cfg), C.byref(out)) == 2
+    assert L.elastic_attn_entries(lns, 1, m, 8, 2, C.byref(cfg), C.byref(out)) == 2
+
+
+def test_block_list_entry_counter_validation():
+    EINVAL, EUNS = 1, 2
+    out = C.c_int64(0)
+    arr = lambda *v: (C.c_int32 * len(v))(*v)  # noqa: E731
+    f = L.elastic_attn_entries_lists
+    rp, ci = arr(0, 1, 2, 2, 3), arr(0, 0, 1)   # 1 sequence x 1 head x 4 query blocks
+    assert f(arr(200), 1, None, 4, 1, 64, 4, rp, ci, C.byref(out)) == 0
+    assert out.value == 4 * (200 * 201 // 2)                                  # all heads full
+    assert f(arr(200), 1, arr(0), 4, 1, 64, 4, rp, ci, C.byref(out)) == 0
+    # query block 0 lists block 0, block 1 lists block 0, block 2 none, block 3 (8 rows) block 1
+    assert out.value == 4 * (64 * 65 // 2 + 64 * 64 + 0 + 8 * 64)
+    assert f(arr(300), 1, arr(0), 4, 1, 64, 4, rp, ci, C.byref(out)) == EINVAL  # 5 query blocks
+    assert f(arr(200), 1, arr(0), 4, 1, 96, 4, rp, ci, C.byref(out)) == EUNS
+    assert f(arr(200), 1, arr(0), 4, 1, 64, 4, arr(0, 2, 1, 2, 3), ci, C.byref(out)) == EINVAL
+    assert f(arr(200), 1, arr(0), 4, 1, 64, 4, None, ci, C.byref(out)) == EINVAL
+    assert f(arr(200), 1, arr(0), 4, 3, 64, 4, rp, ci, C.byref(out)) == EINVAL  # 4 % 3 != 0
+    assert f(arr(-1), 1, arr(0), 4, 1, 64, 4, rp, ci, C.byref(out)) == EINVAL
+
+
+def test_misaligned_tensors_are_rejected():
+    EINVAL = 1
+    odd = C.c_void_p(0x1008)
+    for name in ("q", "k", "v", "o"):
+        assert _attn(**{name: odd}) == EINVAL, name
+    assert _attn_kv(q=odd) == EINVAL
+    assert L.elastic_lse_merge(odd, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 16, 8, 128, None) == EINVAL
+    assert L.elastic_lse_merge(FAKE, FAKE, FAKE, FAKE, odd, FAKE, 0, 16, 8, 128, None) == EINVAL
+    assert L.elastic_route(odd, 0, None, 1, 128, 512, 0, 0, FAKE, 64, FAKE, 8, 0.0, None, FAKE,
+                           FAKE, 1 << 30, None) == EINVAL
+
+
+def test_attention_kernel_argument_layout():
+    """The bf16 attention kernels read their argument struct through the argument-segment
+    pointer at offset 0; the build checks each instance's code-object metadata for that."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_elastic_build", os.path.join(ROOT, "hybrid_sparse_full_elastic_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    obj = os.path.join(b.BUILD_DIR, "attn_bf16.o")
+    if not os.path.exists(obj):
+        pytest.skip("no build objects")
+    meta = b.kernel_metadata(obj)
+    assert b.check_attn_kernargs(meta) == 6          # D 64/128 x three sparse kinds
+    bad = [dict(m) for m in meta]
+    bad[0][".args"] = [{".offset": 8, ".size": 168, ".value_kind": "by_value"}]
+    with pytest.raises(RuntimeError):
+        b.check_attn_kernargs(bad)
+    bad[0][".args"] = [{".offset": 0, ".size": 8, ".value_kind": "global_buffer"},
+                       {".offset": 8, ".size": 168, ".value_kind": "by_value"}]
+    with pytest.raises(RuntimeError):
+        b.check_attn_kernargs(bad)
 
 
 def test_block_list_validation_without_gpu():
