@@ -54,6 +54,29 @@ def assert_f32_close(got, ref, what=""):
     return s
 
 
+def pattern_reach(sparse: dict) -> int:
+    """Tokens a sparse row attends at most besides its own block: sink + window for streaming,
+    the sink, local and diagonal blocks for the block pattern."""
+    if sparse["kind"] == "streaming":
+        return int(sparse["sink"]) + int(sparse["window"])
+    return (int(sparse["sink_blocks"]) + int(sparse["local_blocks"]) + 1) * int(sparse["block"])
+
+
+def survey_rows(w: syn.Workload) -> np.ndarray:
+    """Sorted global token indices of the deterministic full-size sample: per sequence, the
+    first 2 * reach rows (where sink and window edges move), every 16th block of 128 rows, and
+    the last block."""
+    cu = w.cu_seqlens()
+    reach = pattern_reach(w.sparse)
+    return np.concatenate([syn.sample_rows(int(n), reach) + int(cu[b]) for b, n in enumerate(w.seqlens)])
+
+
+def group_edge_heads(n_q_heads: int, n_kv_heads: int) -> list:
+    """The first and the last query head of every KV group."""
+    G = n_q_heads // n_kv_heads
+    return sorted({h for g in range(n_kv_heads) for h in (g * G, g * G + G - 1)})
+
+
 def global_rows(w: syn.Workload, per_seq: int, seed: int = 0) -> np.ndarray:
     """Sorted global token indices: a seeded spread of rows per sequence (first/last included)."""
     cu = w.cu_seqlens()
@@ -61,3 +84,30 @@ def global_rows(w: syn.Workload, per_seq: int, seed: int = 0) -> np.ndarray:
     for b, n in enumerate(w.seqlens):
         out.append(syn.spread_rows(int(n), per_seq, seed + b) + int(cu[b]))
     return np.concatenate(out)
+
+
+def random_lists(seed, batch, hkv, nqb, B, density=0.3, extras=True):
+    """Seeded CSR: each row lists a random subset of key blocks 0..qb (sometimes empty, sometimes
+    without the diagonal, sometimes with a later block that must be ignored)."""
+    rng = np.random.default_rng(seed)
+    rp, ci = [0], []
+    for _ in range(batch * hkv):
+        for qb in range(nqb):
+            kbs = set(np.nonzero(rng.random(qb + 1) < density)[0].tolist())
+            if rng.random() < 0.7:
+                kbs.add(qb)
+            if extras and rng.random() < 0.2 and qb + 1 < nqb:
+                kbs.add(qb + 1)            # a later block: ignored
+            if rng.random() < 0.05:
+                kbs = set()                # the block's rows see nothing
+            ci.extend(sorted(kbs))
+            rp.append(len(ci))
+    return {"kind": "block_list", "block": B, "qblocks": nqb, "row_ptr": rp, "col_idx": ci}
+
+
+def dev_lists(lists):
+    d = dict(lists)
+    d["row_ptr"] = torch.tensor(lists["row_ptr"], dtype=torch.int32, device=DEV)
+    d["col_idx"] = torch.tensor(lists["col_idx"] if lists["col_idx"] else [0], dtype=torch.int32,
+                                device=DEV)
+    return d

@@ -31,31 +31,7 @@ def _gpu():
     torch.cuda.empty_cache()
 
 
-def random_lists(seed, batch, hkv, nqb, B, density=0.3, extras=True):
-    """Seeded CSR: each row lists a random subset of key blocks 0..qb (sometimes empty, sometimes
-    without the diagonal, sometimes with a later block that must be ignored)."""
-    rng = np.random.default_rng(seed)
-    rp, ci = [0], []
-    for _ in range(batch * hkv):
-        for qb in range(nqb):
-            kbs = set(np.nonzero(rng.random(qb + 1) < density)[0].tolist())
-            if rng.random() < 0.7:
-                kbs.add(qb)
-            if extras and rng.random() < 0.2 and qb + 1 < nqb:
-                kbs.add(qb + 1)            # a later block: ignored
-            if rng.random() < 0.05:
-                kbs = set()                # the block's rows see nothing
-            ci.extend(sorted(kbs))
-            rp.append(len(ci))
-    return {"kind": "block_list", "block": B, "qblocks": nqb, "row_ptr": rp, "col_idx": ci}
-
-
-def dev_lists(lists):
-    d = dict(lists)
-    d["row_ptr"] = torch.tensor(lists["row_ptr"], dtype=torch.int32, device=H.DEV)
-    d["col_idx"] = torch.tensor(lists["col_idx"] if lists["col_idx"] else [0], dtype=torch.int32,
-                                device=H.DEV)
-    return d
+random_lists, dev_lists = H.random_lists, H.dev_lists
 
 
 def _draw(seed, T, hq, hkv, D, dtype="bf16", scale=0.5):

@@ -23,7 +23,7 @@ int main() {
   long checked = 0, steady = 0;
   for (int BK : {32, 64}) {
     for (int n : {1, 5, 63, 64, 65, 300, 1000, 1500}) {
-      for (int BT : {1, 7, 32, 36, 64, 256}) {
+      for (int BT : {1, 7, 16, 32, 36, 42, 51, 64, 85, 128, 256}) {
         for (size_t pi = 0; pi <= pats.size(); ++pi) {
           const bool full = pi == pats.size();
           const Pattern p = full ? pats[0] : pats[pi];
