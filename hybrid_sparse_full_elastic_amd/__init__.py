@@ -8,6 +8,7 @@ library is loaded on first use (``lib`` or any call), and that raises if it is m
 """
 from ._binding import (  # noqa: F401
     ABI_VERSION, ElasticError, LIB_PATH, SparseCfg, attn_entries, attn_prefill, attn_prefill_kv,
+    attn_prefill_noalloc,
     attn_workspace_size, block_list_entries, lse_merge, retrieval_scores,
     retrieval_workspace_size, route, route_workspace_size, sparse_cfg, static_assignment,
 )

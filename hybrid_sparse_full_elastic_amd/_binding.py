@@ -23,7 +23,7 @@ class ElasticError(RuntimeError):
         self.status = status
         L = _lib()
         msg = f"{where}: {L.elastic_status_string(status).decode()}"
-        if status == EHIP:
+        if status == EHIP or (status == EWORKSPACE and "noalloc" in where):
             msg += f" ({L.elastic_last_error().decode()})"
         super().__init__(msg)
 
@@ -58,6 +58,9 @@ def _load():
     L.elastic_attn_prefill.restype = C.c_int
     L.elastic_attn_prefill.argtypes = [vp, vp, vp, vp, i32, vp, i32, i64, i32, i32, i32, i32, f32,
                                        vp, C.POINTER(SparseCfg), vp, vp, sz, vp]
+    L.elastic_attn_prefill_noalloc.restype = C.c_int
+    L.elastic_attn_prefill_noalloc.argtypes = [vp, vp, vp, vp, i32, vp, i32, i64, i32, i32, i32, i32,
+                                               f32, vp, C.POINTER(SparseCfg), vp, vp]
     L.elastic_attn_prefill_kv.restype = C.c_int
     L.elastic_attn_prefill_kv.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, i64, i64, i32, i32, i32,
                                           i32, i32, i32, i32, f32, vp, C.POINTER(SparseCfg), vp, vp,
@@ -284,6 +287,36 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                   _stream(stream))
     if st != OK:
         raise ElasticError(st, "elastic_attn_prefill")
+    return out
+
+
+def attn_prefill_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                         cu_seqlens: Optional[torch.Tensor] = None,
+                         max_seqlen: Optional[int] = None, head_mask: Optional[torch.Tensor] = None,
+                         sparse=None, softmax_scale: float = 0.0,
+                         lse: Optional[torch.Tensor] = None, stream=None):
+    """attn_prefill for callers that cannot allocate: no workspace (the library's per-GPU
+    scheduler scratch is used) and the caller provides ``out``.  Calls that overlap on one GPU
+    race on that scratch."""
+    _check_qkv(q, k, v)
+    T, hq, D = q.shape
+    hkv = k.shape[1]
+    if k.shape != (T, hkv, D) or v.shape != (T, hkv, D):
+        raise ValueError("k and v must be [T, n_kv_heads, head_dim] matching q")
+    dev = q.device
+    B = _seq_args(cu_seqlens, T, dev)
+    _check_dev("out", out, q.dtype, q.shape, dev)
+    _check_dev("lse", lse, torch.float32, (hq, T), dev)
+    _check_dev("head_mask", head_mask, torch.int32, (B, hkv), dev)
+    _check_lists(sparse, B, hkv, dev)
+    cfg = sparse_cfg(sparse)
+    st = _lib().elastic_attn_prefill_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), BF16 if q.dtype == torch.bfloat16 else FP32,
+        _ptr(cu_seqlens), B, T, int(max_seqlen if max_seqlen is not None else T), hq, hkv, D,
+        float(softmax_scale), _ptr(head_mask), C.byref(cfg) if cfg is not None else None,
+        _ptr(lse), _stream(stream))
+    if st != OK:
+        raise ElasticError(st, "elastic_attn_prefill_noalloc")
     return out
 
 

@@ -250,7 +250,7 @@ int attn_call(const char* who, const void* q, const void* k, const void* v, void
               int64_t total_k, int32_t max_q, int32_t max_k, int32_t q_pos, int32_t k_pos,
               int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float softmax_scale,
               const int32_t* head_mask, const elastic_sparse_cfg* sparse, float* lse_out,
-              void* workspace, size_t workspace_bytes, void* stream) {
+              void* workspace, size_t workspace_bytes, void* stream, bool validate_only = false) {
   if (batch < 1 || total_q < 0 || total_q > INT32_MAX || total_k < 0 || total_k > INT32_MAX ||
       max_q < 0 || max_k < 0)
     return ELASTIC_EINVAL;
@@ -281,7 +281,7 @@ int attn_call(const char* who, const void* q, const void* k, const void* v, void
   if (max_items > INT32_MAX) return ELASTIC_EUNSUPPORTED;
   const AttnWorkspace lay = attn_layout(max_items, batch);
   if (workspace == nullptr || workspace_bytes < lay.total) return ELASTIC_EWORKSPACE;
-  if (total_q == 0) return ELASTIC_OK;
+  if (total_q == 0 || validate_only) return ELASTIC_OK;
 
   const int G = n_q_heads / n_kv_heads;
   const int BT = tokens_per_item(attn_rows_per_item(dtype), G);
@@ -344,6 +344,76 @@ int elastic_attn_prefill_kv(const void* q, const void* k, const void* v, void* o
                    batch, total_q, total_k, max_seqlen_q, max_seqlen_k, q_pos, k_pos, n_q_heads,
                    n_kv_heads, head_dim, softmax_scale, head_mask, sparse, lse_out, workspace,
                    workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------- allocation-free variant
+// The scheduler's header, work list, tile prefix and cost table of elastic_attn_prefill_noalloc
+// live in this array (one copy per GPU, held until the process ends) instead of a caller
+// workspace.  Nothing in it has to start at zero: the scheduler kernel writes the queue header
+// (and zeroes the claim counters) and every item before the attention kernel reads them, so
+// the contents a previous call left are never read.  Calls that overlap on one GPU share the
+// array and race.
+}  // extern "C"
+
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[ELASTIC_NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device, looked up once per device with that
+// device current.  In host code the array's name is only a stand-in, never a device address.
+int noalloc_scratch(void** out) {
+  constexpr int MAX_DEVICES = 64;
+  static std::mutex mu;
+  static void* addr[MAX_DEVICES] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "elastic_attn_prefill_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= MAX_DEVICES) return ELASTIC_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "elastic_attn_prefill_noalloc: hipGetSymbolAddress");
+    if (p == nullptr) return hip_fail(hipErrorInvalidSymbol, "elastic_attn_prefill_noalloc: scratch");
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return ELASTIC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int elastic_attn_prefill_noalloc(const void* q, const void* k, const void* v, void* o,
+                                 int32_t dtype, const int32_t* cu_seqlens, int32_t batch,
+                                 int64_t total_tokens, int32_t max_seqlen, int32_t n_q_heads,
+                                 int32_t n_kv_heads, int32_t head_dim, float softmax_scale,
+                                 const int32_t* head_mask, const elastic_sparse_cfg* sparse,
+                                 float* lse_out, void* stream) {
+  static const char* who = "elastic_attn_prefill_noalloc";
+  // host-only validation first, against a stand-in workspace of the array's size
+  char stand_in = 0;
+  int st = attn_call(who, q, k, v, o, dtype, cu_seqlens, cu_seqlens, batch, total_tokens,
+                     total_tokens, max_seqlen, max_seqlen, 0, 0, n_q_heads, n_kv_heads, head_dim,
+                     softmax_scale, head_mask, sparse, lse_out, &stand_in,
+                     ELASTIC_NOALLOC_SCRATCH_BYTES, stream, /*validate_only=*/true);
+  if (st == ELASTIC_EWORKSPACE) {
+    snprintf(g_last_error, sizeof(g_last_error),
+             "%s: the problem needs %zu bytes of scheduler scratch; the library holds %zu "
+             "(use elastic_attn_prefill with a caller workspace)", who,
+             elastic_attn_workspace_size(dtype, batch, total_tokens, n_q_heads, n_kv_heads, head_dim),
+             (size_t)ELASTIC_NOALLOC_SCRATCH_BYTES);
+    return st;
+  }
+  if (st != ELASTIC_OK || total_tokens == 0) return st;
+  void* ws = nullptr;
+  st = noalloc_scratch(&ws);
+  if (st != ELASTIC_OK) return st;
+  return attn_call(who, q, k, v, o, dtype, cu_seqlens, cu_seqlens, batch, total_tokens,
+                   total_tokens, max_seqlen, max_seqlen, 0, 0, n_q_heads, n_kv_heads, head_dim,
+                   softmax_scale, head_mask, sparse, lse_out, ws, ELASTIC_NOALLOC_SCRATCH_BYTES,
+                   stream);
 }
 
 int elastic_lse_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,

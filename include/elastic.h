@@ -98,7 +98,8 @@ int elastic_abi_version(void);
 /* Static text for a status code. */
 const char* elastic_status_string(int status);
 
-/* Text of the last ELASTIC_EHIP error on the calling thread ("" if none). */
+/* Text of the last ELASTIC_EHIP error on the calling thread ("" if none), or of the last
+ * ELASTIC_EWORKSPACE from elastic_attn_prefill_noalloc. */
 const char* elastic_last_error(void);
 
 /* Bytes of workspace elastic_route needs for these sizes (device memory, any alignment
@@ -197,6 +198,26 @@ int elastic_attn_prefill_kv(const void* q, const void* k, const void* v, void* o
                             int32_t head_dim, float softmax_scale, const int32_t* head_mask,
                             const elastic_sparse_cfg* sparse, float* lse_out, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): elastic_attn_prefill without a workspace argument.
+ * The scheduler's queue header and work list go to a scratch array that the library holds in
+ * device memory, ELASTIC_NOALLOC_SCRATCH_BYTES on every GPU it runs on, until the process ends;
+ * the call itself allocates nothing.  Every call on a GPU shares that GPU's array, so calls
+ * that overlap on one GPU (other streams, other threads) race: the caller must serialise them.
+ * A problem whose workspace (elastic_attn_workspace_size) exceeds the array returns
+ * ELASTIC_EWORKSPACE before any HIP call, with both sizes in elastic_last_error().  8 MiB holds
+ * about 419,000 work items: one bf16 sequence of up to 3.35M tokens with 32 query / 8 KV heads
+ * (1.67M with 64 / 8).  Arguments, results and other errors as for elastic_attn_prefill.
+ */
+#define ELASTIC_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int elastic_attn_prefill_noalloc(const void* q, const void* k, const void* v, void* o,
+                                 int32_t dtype, const int32_t* cu_seqlens, int32_t batch,
+                                 int64_t total_tokens, int32_t max_seqlen, int32_t n_q_heads,
+                                 int32_t n_kv_heads, int32_t head_dim, float softmax_scale,
+                                 const int32_t* head_mask, const elastic_sparse_cfg* sparse,
+                                 float* lse_out, void* stream);
 
 /*
  * Combines two attention results of the same query rows over disjoint key sets (for example

@@ -316,3 +316,33 @@ def test_retrieval_and_assignment_validation_without_gpu():
     assert a(None, 8, 0.5, FAKE, None) == EINVAL
     assert a(FAKE, 16385, 0.5, FAKE, None) == EUNS
     assert a(None, 0, 0.5, None, None) == 0                  # no units: no-op
+
+
+def _noalloc(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dtype=0, cu=None, batch=1, T=256, maxlen=256, hq=8,
+             hkv=2, D=128, scale=0.0, mask=None, sparse=ext.sparse_cfg({"kind": "streaming", "sink": 4, "window": 64}),
+             lse=None, stream=None)
+    a.update(kw)
+    sp = C.byref(a["sparse"]) if a["sparse"] is not None else None
+    return L.elastic_attn_prefill_noalloc(a["q"], a["k"], a["v"], a["o"], a["dtype"], a["cu"],
+                                          a["batch"], a["T"], a["maxlen"], a["hq"], a["hkv"], a["D"],
+                                          a["scale"], a["mask"], sp, a["lse"], a["stream"])
+
+
+def test_noalloc_validation_without_gpu():
+    """The allocation-free variant validates on the host, and rejects problems whose scheduler
+    scratch exceeds the library's fixed array, before any HIP call."""
+    EINVAL, EUNS, EWS = 1, 2, 3
+    assert _noalloc(q=None) == EINVAL
+    assert _noalloc(o=C.c_void_p(0x1008)) == EINVAL
+    assert _noalloc(hq=6, hkv=4) == EINVAL
+    assert _noalloc(D=96) == EUNS
+    assert _noalloc(T=0, maxlen=0) == 0                      # nothing to do, no HIP call
+    limit = 8 << 20
+    big = 4_000_000                                          # 500,000 items of 32 / 8 heads
+    assert ext.attn_workspace_size(0, 1, big, 32, 8, 128) > limit
+    assert _noalloc(T=big, maxlen=big, hq=32, hkv=8) == EWS
+    msg = L.elastic_last_error().decode()
+    assert "scratch" in msg and str(limit) in msg, msg
+    ok = 3_000_000
+    assert ext.attn_workspace_size(0, 1, ok, 32, 8, 128) <= limit
