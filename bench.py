@@ -38,6 +38,13 @@ def parse():
     p.add_argument("--copy-probe", action="store_true",
                    help="run one plain elementwise kernel first that reads 1 GiB and writes 1 GiB "
                         "(calibrates the HBM byte counters)")
+    p.add_argument("--mask", choices=("workload", "full", "sparse"), default="workload",
+                   help="head mask of the timed attention call: the workload's (router or forced), "
+                        "every head full, or every head sparse (for per-case profiles)")
+    p.add_argument("--window", type=int, default=0,
+                   help="override the streaming window of a streaming workload (0: keep)")
+    p.add_argument("--cpu-seconds-per-config", type=float, default=3.0,
+                   help="oracle sample time for each of the other workload shapes (0: skip them)")
     return p.parse_args()
 
 
@@ -57,6 +64,9 @@ def main():
     dev = "cuda:0"
     w = syn.WORKLOADS[args.workload]
     assert w.dtype == "bf16", "the timed workload is a bf16 layer"
+    if args.window > 0:
+        assert w.sparse["kind"] == "streaming", "--window applies to streaming workloads"
+        w = w.with_(sparse=dict(w.sparse, window=args.window))
 
     def dev_t(x):
         if x.dtype == np.uint16:
@@ -82,6 +92,9 @@ def main():
     if not has_router:
         fm = syn.forced_mask(w)
         mask.copy_(torch.from_numpy(fm))
+    # the timed call's head mask: the router's (or the forced one), or an override
+    attn_mask = {"workload": mask, "full": None,
+                 "sparse": torch.zeros((B, hkv), dtype=torch.int32, device=dev)}[args.mask]
     ws_attn = torch.empty(ext.attn_workspace_size(0, B, T, hq, hkv, D), dtype=torch.uint8, device=dev)
     ws_route = torch.empty(max(1, ext.route_workspace_size(B, T, w.router["d_model"]) if has_router else 1),
                            dtype=torch.uint8, device=dev)
@@ -97,7 +110,7 @@ def main():
                       workspace=ws_route)
         if ev is not None:
             ev[1].record(stream)
-        ext.attn_prefill(q, k, v, cu_seqlens=cu, max_seqlen=w.max_seqlen, head_mask=mask,
+        ext.attn_prefill(q, k, v, cu_seqlens=cu, max_seqlen=w.max_seqlen, head_mask=attn_mask,
                          sparse=w.sparse, out=o, workspace=ws_attn)
         if ev is not None:
             ev[2].record(stream)
@@ -127,8 +140,8 @@ def main():
     attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
     route_ms = [e[0].elapsed_time(e[1]) for e in evs] if has_router else [0.0]
 
-    # work actually done, from the mask the router produced (host closed forms)
-    mask_h = mask.cpu().numpy()
+    # work actually done, from the mask the timed call used (host closed forms)
+    mask_h = (np.ones((B, hkv), dtype=np.int32) if attn_mask is None else attn_mask.cpu().numpy())
     entries = ext.attn_entries(list(w.seqlens), mask_h, hq, hkv, w.sparse)
     flops = 4 * D * entries
     dense = hq * sum(n * (n + 1) // 2 for n in w.seqlens)
@@ -148,6 +161,7 @@ def main():
             "head_dim": D, "sparse": w.sparse,
             "router": {k2: v2 for k2, v2 in (w.router or {}).items()} if has_router else None,
             "head_mask": mask_h.tolist(),
+            "mask_source": args.mask if args.mask != "workload" else ("router" if has_router else "forced"),
             "omega_msr": float((mask_h == 0).mean()),
             "omega_esr": 1.0 - entries / dense,
             "effective_flops": flops,
@@ -184,6 +198,9 @@ def main():
 
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, data, mask_h, args.cpu_seconds)
+        if args.cpu_seconds_per_config > 0:
+            del data
+            rec["cpu_baseline"]["per_config"] = cpu_per_config(w.name, args.cpu_seconds_per_config)
 
     print(json.dumps(rec), flush=True)
 
@@ -207,9 +224,17 @@ def recorded_traffic(workload):
     return int(float(fields["traffic_bytes_per_launch"]))
 
 
-def _time_attn(ext, torch, stream, fn, reps=10, warm=3):
-    for _ in range(warm):
+def _time_attn(ext, torch, stream, fn, reps=10, warm=3, min_warm_ms=50.0):
+    """Mean time of one call over `reps` back-to-back calls, after `warm` calls and at least
+    `min_warm_ms` of warm-up work: a short call timed right after the GPU sat idle (host-side
+    input generation) would otherwise be timed while the clock is still ramping up."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < warm or (time.perf_counter() - t0) * 1e3 < min_warm_ms:
         fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
@@ -392,39 +417,99 @@ def streaming_scaling(ext, torch, stream):
             "window_check_pass": all(1.6 <= r <= 2.2 for r in ratios)}
 
 
-def cpu_baseline(w, data, mask_h, target_s):
-    """The fp64 oracle on the host cores, on a bounded seeded row sample of the workload."""
+def _host_cpu():
+    """(threads the oracle uses, CPUs visible to this process, CPU model).  The oracle's pool is
+    capped at 16 threads: the GPU machine's CPU share for one GPU."""
+    try:
+        visible = len(os.sched_getaffinity(0))
+    except AttributeError:
+        visible = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return max(1, min(visible, 16)), visible, model
+
+
+def _oracle_rows(w, data, mask_h, target_s, cores, seed0=0, rows_per=8):
+    """Seeded row batches of workload w through the attention oracle until target_s of oracle
+    time: returns (seconds, effective FLOPs of the sampled rows, rows)."""
     import oracle
     from synth import inputs as syn
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = max(1, min(cores, 16))
     D = w.head_dim
-    rows_per = 8
-    elapsed, flops, nrows = 0.0, 0, 0
-    seed = 0
+    cu = w.cu_seqlens()
+    elapsed, flops, nrows, seed = 0.0, 0, 0, 0
     while elapsed < target_s and seed < 64:
-        rows = np.concatenate([syn.spread_rows(int(n), rows_per, seed * 131 + b) + int(w.cu_seqlens()[b])
-                               for b, n in enumerate(w.seqlens)])
+        rows = np.concatenate([syn.spread_rows(int(n), rows_per, (seed0 + seed) * 131 + b) + int(cu[b])
+                               for b, n in enumerate(w.seqlens) if n > 0])
         t = time.time()
-        oracle.attention(data["q"], data["k"], data["v"], w.cu_seqlens(), mask_h, w.sparse,
-                         rows=rows, workers=cores)
+        oracle.attention(data["q"], data["k"], data["v"], cu, mask_h, w.sparse, rows=rows,
+                         workers=cores)
         elapsed += time.time() - t
-        cu = w.cu_seqlens()
         seq_of = np.searchsorted(cu, rows, side="right") - 1
         for b in range(w.batch):
             loc = rows[seq_of == b] - cu[b]
+            if len(loc) == 0:
+                continue
             for g in range(w.n_kv_heads):
                 cnt = oracle.row_key_counts(int(w.seqlens[b]), bool(mask_h[b, g]), w.sparse, rows=loc)
                 flops += 4 * D * w.group * int(cnt.sum())
         nrows += len(rows)
         seed += 1
+    return elapsed, flops, nrows
+
+
+def cpu_baseline(w, data, mask_h, target_s):
+    """The fp64 oracle on the host cores, on a bounded seeded row sample of the workload."""
+    cores, visible, model = _host_cpu()
+    elapsed, flops, nrows = _oracle_rows(w, data, mask_h, target_s, cores)
     return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
             "sample": f"{nrows} seeded rows x all {w.n_q_heads} query heads of {w.name} "
-                      f"({elapsed:.1f} s, fp64 numpy, {cores} threads)"}
+                      f"({elapsed:.1f} s, fp64 numpy, {cores} threads)",
+            "cpu_model": model, "cpus_visible": visible}
+
+
+def cpu_per_config(main_name, target_s):
+    """The oracle on each of the other workload shapes, in the workload list's order: router
+    (pooling, MLP, threshold) timed whole where the shape has one, attention on seeded row
+    batches for about target_s, and the whole layer's oracle time extrapolated from the
+    sampled rate (FLOPs over allowed entries)."""
+    import oracle
+    import hybrid_sparse_full_elastic_amd as ext
+    from synth import inputs as syn
+    cores, _, _ = _host_cpu()
+    out = []
+    for name in syn.WORKLOAD_ORDER:
+        if name == main_name:
+            continue
+        w = syn.WORKLOADS[name]
+        rec = {"workload": name}
+        data = syn.make_qkv(w)
+        if w.router is not None:
+            rin = syn.make_router_inputs(w)
+            t = time.time()
+            r = oracle.route(rin["hidden"], w.cu_seqlens(), rin["w1"], rin["w2"], rin["threshold"])
+            rec["router_s"] = round(time.time() - t, 3)
+            mask = r["mask"]
+            del rin
+        elif w.forced_mask is not None and name != "qwen-64k-stream-sweep":
+            mask = syn.forced_mask(w)
+        else:
+            mask = syn.sweep_mask(w.n_kv_heads, 0.5)   # the sparse-fraction sweep's middle point
+        sec, flops, nrows = _oracle_rows(w, data, mask, target_s, cores, seed0=17)
+        total = 4 * w.head_dim * ext.attn_entries(list(w.seqlens), mask, w.n_q_heads, w.n_kv_heads, w.sparse)
+        rate = flops / sec
+        rec.update({"mask": mask.tolist(), "rows_sampled": nrows, "attention_s": round(sec, 3),
+                    "tflops": round(rate / 1e12, 6),
+                    "attention_full_layer_s_extrapolated": round(total / rate, 1)})
+        out.append(rec)
+        del data
+    return out
 
 
 if __name__ == "__main__":

@@ -21,9 +21,10 @@ namespace {
 
 constexpr int PLAN_THREADS = 1024;
 constexpr int PLAN_BUCKETS = 1024;   // cost buckets per queue (see bucket_of)
-constexpr int PLAN_LDS_SEQ = 2048;   // sequences whose lengths / tile offsets are cached in LDS
+constexpr int PLAN_LDS_SEQ = 1024;   // sequences whose lengths / tile offsets are cached in LDS
 constexpr int PLAN_LDS_MASK = 16384; // head-mask entries cached in LDS
 constexpr int PLAN_LDS_COST = 16384; // items whose costs are cached in LDS (else cost_tmp)
+constexpr int PLAN_MEMO_TILES = 4096; // query tiles whose full / sparse costs are tabulated in LDS
 constexpr int ITEM_OVERHEAD = 2;     // per-item cost (prologue, epilogue) in key tiles, for the cut
 
 // Cost bucket: exact below 768 key tiles, then 16 tiles wide; 1023 holds everything above.
@@ -60,6 +61,26 @@ __device__ inline long long block_scan(long long x, long long* tmp, long long* t
   return r;
 }
 
+// One slot of a shared LDS counter per lane: `key` (any value where active is false) is
+// incremented by one for every active lane, and each active lane gets the counter's value
+// before its own increment.  When every active lane of the wave has the same key (items of
+// equal cost in one queue, the common case for sparse heads) one atomic adds them all, which
+// spares the LDS from serialising 64 atomics on one address.  Every lane of the wave calls it.
+__device__ inline int lds_count(int* counters, int key, bool active) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t act = __ballot(active);
+  if (act == 0) return 0;
+  const int leader = __ffsll((unsigned long long)act) - 1;
+  const int k0 = __shfl(key, leader, 64);
+  if (__ballot(active && key == k0) == act) {
+    int base = 0;
+    if (lane == leader) base = atomicAdd(&counters[k0], (int)__popcll(act));
+    base = __shfl(base, leader, 64);
+    return base + (int)__popcll(act & ((1ull << lane) - 1ull));
+  }
+  return active ? atomicAdd(&counters[key], 1) : 0;
+}
+
 // BK (key tile width) is a template argument so that the tile arithmetic of the cost model
 // divides by a constant.
 template <int BK>
@@ -74,6 +95,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
   __shared__ int s_klen[PLAN_LDS_SEQ];  // key rows
   __shared__ unsigned char s_full[PLAN_LDS_MASK];
   __shared__ int s_cost[PLAN_LDS_COST];
+  __shared__ int s_memo[2][PLAN_MEMO_TILES];  // cost of a query tile: [0] sparse heads, [1] full
   const int tid = threadIdx.x;
   const bool seq_cached = batch <= PLAN_LDS_SEQ;
   const bool mask_cached = (int64_t)batch * n_kv_heads <= PLAN_LDS_MASK;
@@ -135,16 +157,18 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     it.seq = seq_of_tile(tile);
     it.qtile = tile - prefix_of(it.seq);
   };
+  auto full_of = [&](const WorkItem& it) -> bool {
+    const int mi = it.seq * n_kv_heads + it.group;
+    return mask_cached ? s_full[mi] != 0 : (head_mask == nullptr || head_mask[mi] != 0);
+  };
   // cost: key tiles of the sequence's key range that the item's queries may see
-  auto cost_of = [&](const WorkItem& it) -> int {
+  auto cost_of_mode = [&](const WorkItem& it, bool full) -> int {
     const int b = it.seq, g = it.group;
     const int n = seq_cached ? s_len[b] : seq_len(b);
     const int nk = seq_cached ? s_klen[b] : key_len(b);
     const int qp = geo.q_pos >= 0 ? geo.q_pos : geo.k_pos + nk - n;  // absolute position of row 0
     const int t0 = it.qtile * BT;
     const int t1 = min(t0 + BT, n) - 1;
-    const int mi = b * n_kv_heads + g;
-    const bool full = mask_cached ? s_full[mi] != 0 : (head_mask == nullptr || head_mask[mi] != 0);
     if (!full && pat.kind == ELASTIC_SPARSE_BLOCK_LIST) {
       // block lists: listed blocks of the item's query blocks (an upper bound of the union)
       const int a0 = qp + t0, a1 = qp + t1;
@@ -159,16 +183,32 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     const KeyTiles kt(full ? MODE_FULL : pat.kind, pat, qp + t0, qp + t1, BK, geo.k_pos, geo.k_pos + nk);
     return kt.count();
   };
+  auto cost_of = [&](const WorkItem& it) -> int { return cost_of_mode(it, full_of(it)); };
 
   // per-item cost (then cost | XCD << 28): in LDS when it fits, else in the workspace
   int* const cost = nitem <= PLAN_LDS_COST ? s_cost : cost_tmp;
 
-  // 2. Costs, and their total weight for the cut.
+  // 2. Costs, and their total weight for the cut.  Every KV head of a query tile shares its
+  //    tile's cost for its mode (except with block lists, which differ per head), so the
+  //    closed forms are evaluated once per (tile, mode) into an LDS table when it fits.
+  const bool memo = pat.kind != ELASTIC_SPARSE_BLOCK_LIST && total_tiles <= PLAN_MEMO_TILES &&
+                    nitem > 2 * PLAN_THREADS;  // below that the extra pass costs what it saves
+  if (memo) {
+    for (int t = tid; t < 2 * total_tiles; t += PLAN_THREADS) {
+      const int tile = t >> 1;
+      WorkItem it;
+      it.seq = seq_of_tile(tile);
+      it.qtile = tile - prefix_of(it.seq);
+      it.group = 0;
+      s_memo[t & 1][tile] = cost_of_mode(it, (t & 1) != 0);
+    }
+    __syncthreads();
+  }
   long long wsum = 0;
   for (int u = tid; u < nitem; u += PLAN_THREADS) {
     WorkItem it;
     locate(u, it);
-    const int c = cost_of(it);
+    const int c = memo ? s_memo[full_of(it) ? 1 : 0][u / n_kv_heads] : cost_of(it);
     cost[u] = c;
     wsum += c + ITEM_OVERHEAD;
   }
@@ -210,15 +250,19 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     long long before = carry + inc - wt;  // line weight before this thread's first position
 #pragma unroll
     for (int r = 0; r < CUT_PT; ++r) {
-      if (uu[r] < 0) continue;
-      const long long w = cc[r] + ITEM_OVERHEAD;
-      const long long mid2 = 2 * before + w;  // twice the item's midpoint
-      before += w;
-      // floor(8 * midpoint / W) in fp64 (a 64-bit integer division costs far more; a boundary
-      // rounded the other way only moves one item to the neighbouring queue)
-      const int x = (int)min((double)(SCHED_NX - 1), floor((double)mid2 * inv_2w));
-      cost[uu[r]] = cc[r] | (x << 28);
-      atomicAdd(&hist[x * PLAN_BUCKETS + (PLAN_BUCKETS - 1 - bucket_of(cc[r]))], 1);
+      const bool active = uu[r] >= 0;
+      int key = 0;
+      if (active) {
+        const long long w = cc[r] + ITEM_OVERHEAD;
+        const long long mid2 = 2 * before + w;  // twice the item's midpoint
+        before += w;
+        // floor(8 * midpoint / W) in fp64 (a 64-bit integer division costs far more; a
+        // boundary rounded the other way only moves one item to the neighbouring queue)
+        const int x = (int)min((double)(SCHED_NX - 1), floor((double)mid2 * inv_2w));
+        cost[uu[r]] = cc[r] | (x << 28);
+        key = x * PLAN_BUCKETS + (PLAN_BUCKETS - 1 - bucket_of(cc[r]));
+      }
+      lds_count(hist, key, active);
     }
     carry += total;
   }
@@ -248,15 +292,21 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
 
   // 5. Scatter.  Order inside a bucket is arbitrary; every item writes disjoint outputs with
   //    a fixed reduction order, so results do not depend on it.
-  for (int u = tid; u < nitem; u += PLAN_THREADS) {
+  for (int base = 0; base < nitem; base += PLAN_THREADS) {  // whole waves call lds_count
+    const int u = base + tid;
+    const bool active = u < nitem;
     WorkItem it;
-    locate(u, it);
-    const int packed = cost[u];
-    const int c = packed & 0x0fffffff;
-    const int x = (int)((unsigned)packed >> 28);
-    const int mi = it.seq * n_kv_heads + it.group;
-    it.full = (mask_cached ? s_full[mi] != 0 : (head_mask == nullptr || head_mask[mi] != 0)) ? 1 : 0;
-    items[atomicAdd(&hist[x * PLAN_BUCKETS + (PLAN_BUCKETS - 1 - bucket_of(c))], 1)] = it;
+    int key = 0;
+    if (active) {
+      locate(u, it);
+      const int packed = cost[u];
+      const int c = packed & 0x0fffffff;
+      const int x = (int)((unsigned)packed >> 28);
+      it.full = full_of(it) ? 1 : 0;
+      key = x * PLAN_BUCKETS + (PLAN_BUCKETS - 1 - bucket_of(c));
+    }
+    const int slot = lds_count(hist, key, active);
+    if (active) items[slot] = it;
   }
   if (tid == 0) {
     sched[0] = nitem;
