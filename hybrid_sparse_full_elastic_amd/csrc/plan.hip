@@ -151,8 +151,12 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     return lo;
   };
   auto prefix_of = [&](int b) { return seq_cached ? s_prefix[b] : tile_prefix[b]; };
+  // u / n_kv_heads: a shift for the usual power-of-two head counts (a runtime division costs
+  // tens of instructions, and this one workgroup is bound by its own VALU work per item)
+  const int hkv_shift = (n_kv_heads & (n_kv_heads - 1)) == 0 ? __builtin_ctz(n_kv_heads) : -1;
+  auto tile_of = [&](int u) { return hkv_shift >= 0 ? u >> hkv_shift : u / n_kv_heads; };
   auto locate = [&](int u, WorkItem& it) {
-    const int tile = u / n_kv_heads;
+    const int tile = tile_of(u);
     it.group = u - tile * n_kv_heads;
     it.seq = seq_of_tile(tile);
     it.qtile = tile - prefix_of(it.seq);
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
   for (int u = tid; u < nitem; u += PLAN_THREADS) {
     WorkItem it;
     locate(u, it);
-    const int c = memo ? s_memo[full_of(it) ? 1 : 0][u / n_kv_heads] : cost_of(it);
+    const int c = memo ? s_memo[full_of(it) ? 1 : 0][tile_of(u)] : cost_of(it);
     cost[u] = c;
     wsum += c + ITEM_OVERHEAD;
   }
@@ -224,22 +228,38 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
   //    with the query tile) and every queue ends on short items.  The XCD goes into the top
   //    bits of cost[u].
   //    Each thread takes CUT_PT consecutive line positions per round, so a round needs one
-  //    block-wide scan.
+  //    block-wide scan; the thread locates its first position with divisions and steps to the
+  //    next ones (query tile, then KV head, then sequence).
   constexpr int CUT_PT = 4;
   carry = 0;
   for (int base = 0; base < nitem; base += PLAN_THREADS * CUT_PT) {
     int uu[CUT_PT], cc[CUT_PT];
     long long wt = 0;  // this thread's weight in the round
+    const int L0 = base + tid * CUT_PT;
+    int b = 0, p0 = 0, nt = 1, g = 0, j = 0;
+    if (L0 < nitem) {
+      b = seq_of_tile(tile_of(L0));
+      p0 = prefix_of(b);
+      nt = prefix_of(b + 1) - p0;  // >= 1: b holds position L0
+      const int rr = L0 - p0 * n_kv_heads;
+      g = rr / nt;
+      j = rr - g * nt;
+    }
 #pragma unroll
     for (int r = 0; r < CUT_PT; ++r) {
-      const int L = base + tid * CUT_PT + r;
       uu[r] = -1;
       cc[r] = 0;
-      if (L < nitem) {
-        const int b = seq_of_tile(L / n_kv_heads);
-        const int p0 = prefix_of(b), nt = prefix_of(b + 1) - p0;
-        const int rr = L - p0 * n_kv_heads;
-        const int g = rr / nt, j = rr - g * nt;
+      if (L0 + r < nitem) {
+        if (r > 0 && ++j == nt) {  // next group, or the next sequence that has query tiles
+          j = 0;
+          if (++g == n_kv_heads) {
+            g = 0;
+            do {
+              p0 += nt;
+              nt = prefix_of(++b + 1) - p0;
+            } while (nt == 0);
+          }
+        }
         const int qt = (j & 1) ? nt - 1 - (j >> 1) : (j >> 1);  // 0, nt-1, 1, nt-2, ...
         uu[r] = (p0 + qt) * n_kv_heads + g;
         cc[r] = cost[uu[r]];
