@@ -437,8 +437,11 @@ __device__ __forceinline__ void attn_item(
       // transposing reads of V_j (landed before the last barrier)
       const uint16_t* vs = vslot + svj * SLOT;
       bf16x8 av[NPV];
+      // P.V fragment i: O block db = i % DB, weights (kb, cc) = i / DB, so that consecutive
+      // MFMAs accumulate into different O blocks (measured 0.5% faster on full heads than four
+      // in a row into one block)
       auto vread = [&](int i) {
-        const int db = i >> 2, kb = (i >> 1) & 1, cc = i & 1;
+        const int db = i % DB, kb = (i / DB) >> 1, cc = (i / DB) & 1;
         const uint16_t* src = vs + v_roff[db] + (kb * 32 + cc * 16) * D;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 8 * D));
@@ -538,7 +541,7 @@ __device__ __forceinline__ void attn_item(
 #pragma unroll
         for (int i = 0; i < NPV; ++i) {
           if (i + 4 < NPV) vread(i + 4);
-          const int db = i >> 2, kb = (i >> 1) & 1, cc = i & 1;
+          const int db = i % DB, kb = (i / DB) >> 1, cc = (i / DB) & 1;
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], pop[kb][cc], oacc[db], 0, 0, 0);
           // the first K fragments of tile j+2, after the last V reads
           if (i >= NPV - NPRE)
