@@ -91,8 +91,8 @@ __device__ inline float max3f(float a, float b, float c) {
 
 // An empty statement that takes the values in registers: the computations producing them stay
 // above it.
-__device__ __forceinline__ void keep_here(const bf16x8 (&p)[2][2], const float l) {
-  asm volatile("" ::"v"(p[0][0]), "v"(p[0][1]), "v"(p[1][0]), "v"(p[1][1]), "v"(l));
+__device__ __forceinline__ void keep_here(const bf16x8 (&p0)[2], const bf16x8 (&p1)[2], const float l) {
+  asm volatile("" ::"v"(p0[0]), "v"(p0[1]), "v"(p1[0]), "v"(p1[1]), "v"(l));
 }
 __device__ __forceinline__ void lds_wait_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -396,6 +396,34 @@ __device__ __forceinline__ void attn_item(
     }
     if (tiles.needs_mask(kt_cur)) apply_mask(s0, kt_cur);
     first_max(s0);
+    // The weights of a tile are made in two halves: pairs 0-7 (keys 0-31) during the P.V
+    // MFMAs of the step before, pairs 8-15 (keys 32-63) during its own Q.K^T MFMAs, so both
+    // MFMA regions carry half of the softmax VALU work (measured 0.8% faster on full heads
+    // than all of it in the Q.K^T region, where the P.V region left the VALU idle).
+    // phalf: the first half (P fragments of keys 0-31), ls_half its row sum.
+    bf16x8 phalf[2];
+    float ls_half;
+    auto weight_pair = [&](const f32x16 (&s)[2], int pair, float nm, bf16x8 (&ph)[2], bf16x8 (&p1)[2]) {
+      const int kb = pair >> 3, e = (pair & 7) * 2;
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][e], c, nm));
+      const float pq = __builtin_amdgcn_exp2f(fmaf(s[kb][e + 1], c, nm));
+      const bf16x2 pp = {(__bf16)p0, (__bf16)pq};
+      bf16x8& dst = kb == 0 ? ph[e >> 3] : p1[e >> 3];
+      dst[e & 7] = pp[0];
+      dst[(e & 7) + 1] = pp[1];
+      return pp;
+    };
+    {
+      const float nm = -m_sc;
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+      bf16x8 unused[2];
+#pragma unroll
+      for (int pair = 0; pair < 8; ++pair) {
+        const bf16x2 pp = weight_pair(s0, pair, nm, phalf, unused);
+        ls_half = pair == 0 ? __builtin_amdgcn_fdot2_f32_bf16(pp, ones, 0.f, false)
+                            : __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls_half, false);
+      }
+    }
     int skj = 0, svj = 0;  // LDS slots of K_j and V_j
     // the first K fragments of step 0 (tile 1)
     bf16x8 kpre[NPRE];
@@ -423,17 +451,16 @@ __device__ __forceinline__ void attn_item(
       const int sv2 = svj == 0 ? NSV - 1 : svj - 1;
       const int n_dma = STEADY ? 2 * CPT : (kt_n4 >= 0 ? CPT : 0) + (kt_n2 >= 0 ? CPT : 0);
       const bool has_next = STEADY || kt_n1 >= 0;
-      // Region 1: Q.K^T of tile j+1 (NQK MFMAs; K fragments read five ahead) with the exp2,
-      // bf16 packing and row sums of tile j placed between them; the DMA is issued halfway
-      // (measured: 1.6% faster on full heads than right after the first MFMAs), and the
-      // first V fragments of region 2 are read during the last MFMAs.
+      // Region 1: Q.K^T of tile j+1 (NQK MFMAs; K fragments read five ahead) with the second
+      // half of tile j's exp2 / bf16 packing / row sums (pairs 8-15) placed between them; the
+      // DMA is issued halfway (measured: 1.6% faster on full heads than right after the first
+      // MFMAs), and the first V fragments of region 2 are read during the last MFMAs.
       constexpr int NQK = 2 * DC, NPV = 4 * DB;
-      constexpr int PPM = 16 / NQK;  // weight pairs per Q.K^T MFMA
+      constexpr int QPP = NQK / 8;   // Q.K^T MFMAs per weight pair of the second half
       constexpr int AHEAD = 5;
-      bf16x8 pop[2][2];
-      // row sum of the tile's weights: one dependent chain (the dot2 steps sit one per
-      // MFMA, far enough apart to hide their latency; no combining adds)
-      float ls = 0.f;
+      bf16x8 pop1[2];  // P fragments of keys 32-63 of tile j
+      // row sum of the tile's weights: one dependent chain on from the first half's sum
+      float ls = ls_half;
       // transposing reads of V_j (landed before the last barrier)
       const uint16_t* vs = vslot + svj * SLOT;
       bf16x8 av[NPV];
@@ -447,10 +474,10 @@ __device__ __forceinline__ void attn_item(
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 8 * D));
         av[i] = __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
       };
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
       {
         const uint16_t* ks = kslot + sk1 * SLOT;
         const float nm = -m_sc;
-        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
         const f32x16 zero = {};
         bf16x8 a[NQK];
 #pragma unroll
@@ -463,24 +490,9 @@ __device__ __forceinline__ void attn_item(
           if (i + AHEAD < NQK)
             a[i + AHEAD] = *reinterpret_cast<const bf16x8*>(ks + ((i + AHEAD) & 1) * 32 * D + k_roff[(i + AHEAD) >> 1]);
           sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], qreg[i >> 1], i < 2 ? zero : sn[i & 1], 0, 0, 0);
-#pragma unroll
-          for (int u = 0; u < PPM; ++u) {
-            const int pair = i * PPM + u;
-            const int kb = pair >> 3, e = (pair & 7) * 2;
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], c, nm));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][e + 1], c, nm));
-            const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
-            pop[kb][e >> 3][e & 7] = pp[0];
-            pop[kb][e >> 3][(e & 7) + 1] = pp[1];
-            if (pair == 0) {
-              // the first pair of the row sum: the three-operand form with an inline zero
-              // addend (the accumulating form needs a v_mov of zero first)
-              float r0;
-              asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r0) : "v"(__builtin_bit_cast(uint32_t, pp)), "s"(0x3f803f80u));
-              ls = r0;
-            } else {
-              ls = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls, false);
-            }
+          if (i % QPP == QPP - 1) {
+            const bf16x2 pp = weight_pair(sc, 8 + i / QPP, nm, phalf, pop1);
+            ls = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls, false);
           }
           // the first V fragments of region 2, during the last MFMAs
           if (i >= NQK - NVPRE) vread(i - (NQK - NVPRE));
@@ -497,7 +509,7 @@ __device__ __forceinline__ void attn_item(
         }
       }
       // keep tile j's weights in this region (no sinking past the mask branch)
-      keep_here(pop, ls);
+      keep_here(phalf, pop1, ls);
       // The weights of tile j used the running maximum m.  A row whose partial sum passes
       // 2^70 (some weight above 2^64: the first tiles of a row, or a sharp rise of its scores)
       // is redone with the tile's own maximum; inf and NaN sums take the same path.
@@ -519,30 +531,42 @@ __device__ __forceinline__ void attn_item(
 #pragma unroll
           for (int e = 0; e < 16; ++e) oacc[db][e] *= al;
         const float nm = -m_sc;
-        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
         ls = 0.f;
 #pragma unroll
         for (int pair = 0; pair < 16; ++pair) {
-          const int kb = pair >> 3, e = (pair & 7) * 2;
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], c, nm));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][e + 1], c, nm));
-          const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
-          pop[kb][e >> 3][e & 7] = pp[0];
-          pop[kb][e >> 3][(e & 7) + 1] = pp[1];
+          const bf16x2 pp = weight_pair(sc, pair, nm, phalf, pop1);
           ls = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls, false);
         }
       }
       if (!STEADY && has_next && tiles.needs_mask(kt_n1)) apply_mask(sn, kt_n1);
-      // Region 2: P.V of tile j (NPV MFMAs; transposing V reads four fragments ahead).
+      // Region 2: P.V of tile j (NPV MFMAs; transposing V reads four fragments ahead) with the
+      // first half of tile j+1's weights (pairs 0-7) between them: a pair goes into phalf once
+      // the MFMAs that read tile j's fragment there are issued (fragment cc of the first half
+      // is read by MFMAs cc*DB .. cc*DB + DB - 1).  After the last step these are made from a
+      // tile that does not exist and are never used.
       {
         const uint16_t* kn = kslot + sk2 * SLOT;
+        const float nm = -m_sc;
+        float lsn = 0.f;
+        auto slot_of = [](int p) {  // the P.V MFMA after which pair p of the next tile is made
+          return p < 4 ? DB - 1 + p : 2 * DB - 1 + (p - 4) * ((NPV - 2 * DB) / 4);
+        };
 #pragma unroll
         for (int i = NVPRE; i < 4; ++i) vread(i);
 #pragma unroll
         for (int i = 0; i < NPV; ++i) {
           if (i + 4 < NPV) vread(i + 4);
           const int db = i % DB, kb = (i / DB) >> 1, cc = (i / DB) & 1;
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], pop[kb][cc], oacc[db], 0, 0, 0);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], kb == 0 ? phalf[cc] : pop1[cc], oacc[db], 0, 0, 0);
+#pragma unroll
+          for (int p = 0; p < 8; ++p) {
+            if (slot_of(p) == i) {
+              bf16x8 unused[2];
+              const bf16x2 pp = weight_pair(sn, p, nm, phalf, unused);
+              lsn = p == 0 ? __builtin_amdgcn_fdot2_f32_bf16(pp, ones, 0.f, false)
+                           : __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsn, false);
+            }
+          }
           // the first K fragments of tile j+2, after the last V reads
           if (i >= NPV - NPRE)
             kpre[i - (NPV - NPRE)] =
@@ -550,6 +574,7 @@ __device__ __forceinline__ void attn_item(
           __builtin_amdgcn_sched_barrier(0);
         }
         l_run += ls;
+        ls_half = lsn;
       }
       const int kt_n5 = STEADY ? kt_n4 + 1 : (kt_n4 >= 0 ? tiles.next(kt_n4 + 1) : -1);
       // this step's DMA may stay in flight; the previous step's (K_{j+3}, V_{j+1}) must land
