@@ -32,26 +32,39 @@ __device__ inline int bucket_of(int cost) {
   return cost < 768 ? cost : min(768 + ((cost - 768) >> 4), PLAN_BUCKETS - 1);
 }
 
-// Block-wide inclusive scan of one value per thread (64-bit): wave scans by shuffles, then a
-// scan of the wave totals.  Returns the thread's inclusive prefix and leaves the block total
-// in *total.  Every thread must call it; tmp holds PLAN_THREADS / 64 values.
+// x of the lane that the DPP control CTRL names (0 where it names none, and in the rows that
+// ROWS leaves out), both 32-bit halves moved alike.
+template <int CTRL, int ROWS>
+__device__ inline long long dpp_take(long long x) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, ROWS, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(x >> 32), CTRL, ROWS, 0xf, false);
+  return (long long)(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+// Inclusive scan over the 64 lanes of a wave: Kogge-Stone inside each 16-lane row (row_shr 1,
+// 2, 4, 8), then the total of row 0 into rows 1 and 3 (row_bcast:15) and of rows 0-1 into
+// rows 2 and 3 (row_bcast:31).  DPP moves are VALU operations, where a shuffle is an LDS
+// round trip; the scheduler's single workgroup runs a chain of these scans.
+__device__ inline long long wave_scan(long long x) {
+  x += dpp_take<0x111, 0xf>(x);
+  x += dpp_take<0x112, 0xf>(x);
+  x += dpp_take<0x114, 0xf>(x);
+  x += dpp_take<0x118, 0xf>(x);
+  x += dpp_take<0x142, 0xa>(x);
+  x += dpp_take<0x143, 0xc>(x);
+  return x;
+}
+
+// Block-wide inclusive scan of one value per thread (64-bit): wave scans, then a scan of the
+// wave totals.  Returns the thread's inclusive prefix and leaves the block total in *total.
+// Every thread must call it; tmp holds PLAN_THREADS / 64 values.
 constexpr int PLAN_WAVES = PLAN_THREADS / 64;
 __device__ inline long long block_scan(long long x, long long* tmp, long long* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const long long y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+  x = wave_scan(x);
   if (lane == 63) tmp[w] = x;
   __syncthreads();
   if (w == 0) {
-    long long t = lane < PLAN_WAVES ? tmp[lane] : 0;
-#pragma unroll
-    for (int off = 1; off < PLAN_WAVES; off <<= 1) {
-      const long long y = __shfl_up(t, off, 64);
-      if (lane >= off) t += y;
-    }
+    const long long t = wave_scan(lane < PLAN_WAVES ? tmp[lane] : 0);
     if (lane < PLAN_WAVES) tmp[lane] = t;
   }
   __syncthreads();
@@ -70,20 +83,22 @@ __device__ inline int lds_count(int* counters, int key, bool active) {
   const int lane = threadIdx.x & 63;
   const uint64_t act = __ballot(active);
   if (act == 0) return 0;
-  const int leader = __ffsll((unsigned long long)act) - 1;
-  const int k0 = __shfl(key, leader, 64);
+  const int leader = __ffsll((unsigned long long)act) - 1;  // wave-uniform
+  const int k0 = __builtin_amdgcn_readlane(key, leader);
   if (__ballot(active && key == k0) == act) {
     int base = 0;
     if (lane == leader) base = atomicAdd(&counters[k0], (int)__popcll(act));
-    base = __shfl(base, leader, 64);
+    base = __builtin_amdgcn_readlane(base, leader);
     return base + (int)__popcll(act & ((1ull << lane) - 1ull));
   }
   return active ? atomicAdd(&counters[key], 1) : 0;
 }
 
 // BK (key tile width) is a template argument so that the tile arithmetic of the cost model
-// divides by a constant.
-template <int BK>
+// divides by a constant.  SMALL (the host's choice: the sequences, the head mask and the item
+// bound all fit the LDS caches) makes every cached read an LDS instruction; with the caches
+// chosen at run time the compiler merges the two sources into generic (flat) loads.
+template <int BK, bool SMALL>
 __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     SeqGeom geo, int batch, int n_kv_heads, const int32_t* __restrict__ head_mask, Pattern pat,
     int BT, int64_t max_items, int32_t* __restrict__ tile_prefix,
@@ -97,8 +112,8 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
   __shared__ int s_cost[PLAN_LDS_COST];
   __shared__ int s_memo[2][PLAN_MEMO_TILES];  // cost of a query tile: [0] sparse heads, [1] full
   const int tid = threadIdx.x;
-  const bool seq_cached = batch <= PLAN_LDS_SEQ;
-  const bool mask_cached = (int64_t)batch * n_kv_heads <= PLAN_LDS_MASK;
+  const bool seq_cached = SMALL || batch <= PLAN_LDS_SEQ;
+  const bool mask_cached = SMALL || (int64_t)batch * n_kv_heads <= PLAN_LDS_MASK;
 
   auto seq_len = [&](int b) -> int {
     return geo.cu_q ? geo.cu_q[b + 1] - geo.cu_q[b] : (int)geo.total_q;
@@ -138,6 +153,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
   __syncthreads();
   int64_t count = (int64_t)total_tiles * n_kv_heads;
   if (count > max_items) count = max_items;  // cannot happen for consistent cu_seqlens
+  if (SMALL && count > PLAN_LDS_COST) count = PLAN_LDS_COST;  // max_items bounds it
   const int nitem = (int)count;
 
   // Item u = tile * n_kv_heads + g, tile = tile_prefix[b] + qtile.
@@ -190,7 +206,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
   auto cost_of = [&](const WorkItem& it) -> int { return cost_of_mode(it, full_of(it)); };
 
   // per-item cost (then cost | XCD << 28): in LDS when it fits, else in the workspace
-  int* const cost = nitem <= PLAN_LDS_COST ? s_cost : cost_tmp;
+  int* const cost = SMALL || nitem <= PLAN_LDS_COST ? s_cost : cost_tmp;
 
   // 2. Costs, and their total weight for the cut.  Every KV head of a query tile shares its
   //    tile's cost for its mode (except with block lists, which differ per head), so the
@@ -340,12 +356,16 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
 hipError_t launch_plan(const SeqGeom& geo, int batch, int n_kv_heads, const int32_t* head_mask,
                        const Pattern& pat, int BT, int BK, int64_t max_items, int32_t* tile_prefix,
                        int32_t* cost_tmp, WorkItem* items, int32_t* sched, hipStream_t stream) {
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, geo, batch, n_kv_heads,
+                       head_mask, pat, BT, max_items, tile_prefix, cost_tmp, items, sched);
+  };
+  const bool small = batch <= PLAN_LDS_SEQ && (int64_t)batch * n_kv_heads <= PLAN_LDS_MASK &&
+                     max_items <= PLAN_LDS_COST;
   if (BK == BF16_BK)
-    hipLaunchKernelGGL(plan_kernel<BF16_BK>, dim3(1), dim3(PLAN_THREADS), 0, stream, geo, batch,
-                       n_kv_heads, head_mask, pat, BT, max_items, tile_prefix, cost_tmp, items, sched);
+    small ? launch(plan_kernel<BF16_BK, true>) : launch(plan_kernel<BF16_BK, false>);
   else if (BK == F32_BK)
-    hipLaunchKernelGGL(plan_kernel<F32_BK>, dim3(1), dim3(PLAN_THREADS), 0, stream, geo, batch,
-                       n_kv_heads, head_mask, pat, BT, max_items, tile_prefix, cost_tmp, items, sched);
+    small ? launch(plan_kernel<F32_BK, true>) : launch(plan_kernel<F32_BK, false>);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
