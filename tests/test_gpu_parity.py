@@ -80,7 +80,7 @@ def test_small_bf16_every_element(case):
     cu = np.concatenate([[0], np.cumsum(seqlens)])
     ro, rl = oracle.attention(data["q"], data["k"], data["v"], cu, mask, sparse)
     H.assert_bf16_close(o, ro, name)
-    np.testing.assert_allclose(lse, rl, rtol=0, atol=2e-3)
+    np.testing.assert_allclose(lse, rl, rtol=0, atol=H.BF16_LSE_ATOL)
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -176,7 +176,7 @@ def _sampled_attention(w, data, mask, heads=None, lse=True):
                               rows=rows, heads=hs, workers=16)
     H.assert_bf16_close(o[rows][:, hs], ro, f"{w.name} mask={np.asarray(mask).tolist()}")
     if lse:
-        np.testing.assert_allclose(l[hs][:, rows], rl, rtol=0, atol=2e-3)
+        np.testing.assert_allclose(l[hs][:, rows], rl, rtol=0, atol=H.BF16_LSE_ATOL)
     return o, l
 
 

@@ -93,7 +93,7 @@ def run_case(c: dict) -> None:
             f"mask={c['mask'].tolist()} sparse={ {k: v for k, v in sp.items() if k not in ('row_ptr', 'col_idx')} }")
     if c["dtype"] == "bf16":
         H.assert_bf16_close(got, ro, what)
-        atol = 2e-3
+        atol = H.BF16_LSE_ATOL
     else:
         H.assert_f32_close(got, ro, what)
         atol = 1e-5
