@@ -66,7 +66,7 @@ def pattern_reach(sparse: dict) -> int:
     return (int(sparse["sink_blocks"]) + int(sparse["local_blocks"]) + 1) * int(sparse["block"])
 
 
-def survey_rows(w: syn.Workload) -> np.ndarray:
+def sample_rows_global(w: syn.Workload) -> np.ndarray:
     """Sorted global token indices of the deterministic full-size sample: per sequence, the
     first 2 * reach rows (where sink and window edges move), every 16th block of 128 rows, and
     the last block."""

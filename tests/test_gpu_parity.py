@@ -169,7 +169,7 @@ def _check_router(w, rin, logits, mask, band=1e-3):
 
 def _sampled_attention(w, data, mask, heads=None, lse=True):
     o, l = _run_attn(data, list(w.seqlens), mask, w.sparse, lse=lse)
-    rows = H.survey_rows(w)
+    rows = H.sample_rows_global(w)
     hs = list(range(w.n_q_heads)) if heads is None else heads
     print(f"[sample] {w.name}: {len(rows)} rows x {len(hs)} heads", flush=True)
     ro, rl = oracle.attention(data["q"], data["k"], data["v"], w.cu_seqlens(), mask, w.sparse,
