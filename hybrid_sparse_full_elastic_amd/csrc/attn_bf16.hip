@@ -37,14 +37,14 @@
 //    range.  Tiles are unpadded with XOR swizzles of the 16-byte chunks chosen so the K row
 //    reads and the transposing V reads are free of LDS bank conflicts.
 //  * Per tile step j, two instruction regions fenced with sched_barrier so the issue order is
-//    the written one: the Q.K^T MFMAs of tile j+1 with the exp2 / bf16 packing / row sums of
-//    tile j between them (K fragments read five MFMAs ahead, the step's DMA issued halfway,
-//    the first V fragments read during the last MFMAs), then the P.V MFMAs of tile j with
-//    the transposing V reads (four ahead) between them and, after them, the first K
-//    fragments of tile j+2 (it landed one barrier early), so the next step starts on MFMAs.
-//    A wave keeps its MFMA pipe fed while its own softmax work issues beside it, and the two
-//    waves sharing a SIMD fill each other's gaps.  The mask of an edge tile sits between the
-//    regions; one barrier per step.
+//    the written one: the Q.K^T MFMAs of tile j+1 with the second half of tile j's exp2 /
+//    bf16 packing / row sums between them (K fragments read five MFMAs ahead, the step's DMA
+//    issued halfway, the first V fragments read during the last MFMAs), then the P.V MFMAs of
+//    tile j with the transposing V reads (four ahead) and the first half of tile j+1's
+//    weights between them and, after them, the first K fragments of tile j+2 (it landed one
+//    barrier early), so the next step starts on MFMAs.  Both regions carry half of the
+//    softmax work, and the two waves sharing a SIMD fill each other's gaps.  The mask of an
+//    edge tile sits between the regions; one barrier per step.
 //  * Persistent grid: each workgroup claims items from its XCD's queue; the next item is
 //    claimed in the current item's prologue and its descriptor copied to LDS meanwhile.
 //  * Epilogue: each wave stages its 32 normalised rows in the idle tile slots (same swizzle) and
