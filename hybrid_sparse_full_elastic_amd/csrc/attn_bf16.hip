@@ -372,7 +372,9 @@ __device__ __forceinline__ void attn_item(
     else if (n_after == 4) WAIT_VMCNT(4 * CPT);
     else if (n_after == 3) WAIT_VMCNT(3 * CPT);
     else WAIT_VMCNT(CPT);
-    __syncthreads();  // K_0 is in LDS, and every wave has read this item's claim: the slot is free
+    // K_0 is in LDS, and every wave has read this item's claim: the slot is free.  An LDS-only
+    // barrier: __syncthreads would also wait for every copy still in flight
+    lds_wait_barrier();
     int next_idx = 0;  // thread 0
     if (tid == 0) {
       next_idx = k_next < cl.len ? cl.q0 + k_next : claim_item(sched);
@@ -386,7 +388,7 @@ __device__ __forceinline__ void attn_item(
     if (kt_n3 >= 0) WAIT_VMCNT(2 * CPT);
     else if (kt_n1 >= 0) WAIT_VMCNT(CPT);
     else WAIT_VMCNT(0);
-    __syncthreads();
+    lds_wait_barrier();
     if (wave == 0) {
       // the next item's descriptor goes global -> LDS by DMA (4 lanes x 4 bytes) and lands
       // during the tile steps, whose copy waits retire it
