@@ -195,6 +195,7 @@ def main():
         torch.cuda.empty_cache()
         if not args.no_scaling:
             rec["supplements"]["streaming_scaling"] = streaming_scaling(ext, torch, stream)
+        rec["supplements"]["reference_gemm"] = reference_gemm(torch, stream)
 
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, data, mask_h, args.cpu_seconds)
@@ -309,6 +310,22 @@ def deployment(ext, torch, w, q, k, v, o, mask, ws, stream):
             "block_lists_sel8_all_heads_tflops": round(4 * D * ent_sel / ms_sel / 1e9, 2),
             "block_lists_sel8_router_mask_ms": round(ms_selm, 4),
             "block_lists_sel8_router_mask_tflops": round(4 * D * ent_selm / ms_selm / 1e9, 2)}
+
+
+def reference_gemm(torch, stream):
+    """For scale only, not part of the path: torch's bf16 matmul (the vendor GEMM library) on
+    square problems on the same GPU, as a practical dense-MFMA rate beside the 2.5 PF datasheet
+    figure."""
+    out = {}
+    for n in (8192, 16384):
+        a = torch.randn((n, n), device="cuda:0").to(torch.bfloat16)
+        b = torch.randn((n, n), device="cuda:0").to(torch.bfloat16)
+        ms = _time_attn(None, torch, stream, lambda: torch.matmul(a, b), reps=10 if n == 8192 else 4)
+        out[f"matmul_bf16_{n}_ms"] = round(ms, 4)
+        out[f"matmul_bf16_{n}_tflops"] = round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+        del a, b
+    torch.cuda.empty_cache()
+    return out
 
 
 def static_assignment_detail(ext, torch, w, q, k, stream):
