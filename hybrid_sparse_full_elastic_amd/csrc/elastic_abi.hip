@@ -87,7 +87,7 @@ AttnWorkspace attn_layout(int64_t max_items, int32_t batch) {
 // ---------------------------------------------------------------- router sizing
 struct RouteWorkspace {
   int64_t max_slabs;
-  size_t partials, zpart, total;
+  size_t partials, zpart, done, total;
 };
 
 RouteWorkspace route_layout(int32_t batch, int64_t total_tokens, int32_t d_model) {
@@ -96,7 +96,8 @@ RouteWorkspace route_layout(int32_t batch, int64_t total_tokens, int32_t d_model
   const size_t strips = (size_t)(d_model + ROUTE_HCOLS - 1) / ROUTE_HCOLS;
   w.partials = 0;
   w.zpart = align_up((size_t)w.max_slabs * d_model * sizeof(float));
-  w.total = align_up(w.zpart + (size_t)batch * strips * ROUTE_MAX_DR * sizeof(float));
+  w.done = align_up(w.zpart + (size_t)batch * strips * ROUTE_MAX_DR * sizeof(float));
+  w.total = align_up(w.done + (size_t)batch * sizeof(int32_t));
   return w;
 }
 
@@ -226,7 +227,8 @@ int elastic_route(const void* hidden, int32_t hidden_dtype, const int32_t* cu_se
       hidden, hidden_dtype, cu_seqlens, batch, total_tokens, d_model, pool_head, pool_tail, w1,
       d_router, w2, n_kv_heads, threshold, logits_out, mask_out,
       reinterpret_cast<float*>(ws + lay.partials), total_tokens > 0 ? lay.max_slabs : 0,
-      reinterpret_cast<float*>(ws + lay.zpart), static_cast<hipStream_t>(stream));
+      reinterpret_cast<float*>(ws + lay.zpart), reinterpret_cast<int32_t*>(ws + lay.done),
+      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ELASTIC_OK : hip_fail(e, "elastic_route");
 }
 

@@ -407,7 +407,7 @@ hipError_t launch_route(const void* hidden, int hidden_dtype, const int32_t* cu_
                         int64_t total_tokens, int d_model, int pool_head, int pool_tail,
                         const float* w1, int d_router, const float* w2, int n_kv_heads,
                         float threshold, float* logits_out, int32_t* mask_out, float* partials,
-                        int64_t max_slabs, float* zpart, hipStream_t stream);
+                        int64_t max_slabs, float* zpart, int32_t* done, hipStream_t stream);
 constexpr int ROUTE_HCOLS = 64;  // columns per route_strip workgroup
 
 }  // namespace elastic

@@ -10,7 +10,7 @@
 // Pooling streams hidden[T, d] once from HBM and dominates the router's time, so it is
 // written for bandwidth: many workgroups, each summing a slab of up to ROUTE_SLAB rows of a
 // 512-column strip with 16-byte loads, waves interleaving rows; the workgroup shape follows
-// the number of slabs (launch_route).  Two small kernels finish the mean, the MLP and the
+// the number of slabs (launch_route).  One small kernel finishes the mean, the MLP and the
 // threshold.  No floating-point atomics anywhere: every sum runs in a fixed order, so results
 // are bitwise reproducible.
 #include "elastic_internal.hpp"
@@ -155,8 +155,11 @@ __device__ inline void load8(const void* hidden, int dtype, int64_t off, float* 
 // with four rows in flight per lane (many slabs: about eight such workgroups per CU stream).
 __global__ __launch_bounds__(256) void route_pool_partial(
     const void* __restrict__ hidden, int dtype, const int32_t* __restrict__ cu, int batch,
-    int64_t total, int d, int pool_head, int pool_tail, int slab_rows, float* __restrict__ partials) {
+    int64_t total, int d, int pool_head, int pool_tail, int slab_rows, float* __restrict__ partials,
+    int32_t* __restrict__ done) {
   __shared__ float red[3][64][8 + 1];
+  if (blockIdx.x == 0 && blockIdx.y == 0)  // route_strip's completion counters
+    for (int i = threadIdx.x; i < batch; i += blockDim.x) done[i] = 0;
   const int slab = blockIdx.x;
   int b, slab_in;
   find_slab(cu, batch, total, pool_head, pool_tail, slab_rows, slab, false, &b, &slab_in);
@@ -207,11 +210,14 @@ __global__ __launch_bounds__(256) void route_pool_partial(
 template <int DT>
 __global__ __launch_bounds__(512) void route_pool_partial_1r(
     const void* __restrict__ hidden, const int32_t* __restrict__ cu, int batch, int64_t total,
-    int d, int pool_head, int pool_tail, int slab_rows, float* __restrict__ partials) {
+    int d, int pool_head, int pool_tail, int slab_rows, float* __restrict__ partials,
+    int32_t* __restrict__ done) {
   constexpr int RW = 8, RIF = 16;
   constexpr bool BF = DT == ELASTIC_BF16;
   constexpr int esz = BF ? 2 : 4;
   __shared__ float red[RW - 1][64][8 + 1];
+  if (blockIdx.x == 0 && blockIdx.y == 0)  // route_strip's completion counters
+    for (int i = threadIdx.x; i < batch; i += blockDim.x) done[i] = 0;
   const int slab = blockIdx.x;
   int b, slab_in;
   find_slab(cu, batch, total, pool_head, pool_tail, slab_rows, slab, false, &b, &slab_in);
@@ -271,21 +277,63 @@ __global__ __launch_bounds__(512) void route_pool_partial_1r(
 
 // route_strip: workgroup (b, ch) finishes the mean of sequence b over HCOLS columns (the
 // sequence's slab partials summed in slab order) and multiplies that strip into every row of
-// W1 (partial z).  route_finish (one workgroup per sequence) sums the partial z in strip order,
-// applies ReLU and W2 and thresholds the logits.  The kernel boundary makes the partial z
-// visible: a completion counter inside one kernel needs a device-scope fence per workgroup,
-// which writes back the L2 and measured about 17 us.  All floating-point sums run in a fixed
-// order.
+// W1 (partial z).  The last of the sequence's nch workgroups to finish -- a completion count
+// per sequence, zeroed by the pooling kernel -- then sums the partial z in strip order, applies
+// ReLU and W2 and thresholds the logits.  One device-scope release per workgroup makes its
+// partial z visible (64 workgroups per sequence at d = 4096, each with 256 bytes to write
+// back; a count over the pooling kernel's workgroups, each with a slab of partial sums, cost
+// about 17 us).  All floating-point sums run in a fixed order.
 constexpr int HCOLS = ROUTE_HCOLS;
 constexpr int HT = 1024;          // threads of route_strip: 16 waves split a sequence's slabs
 constexpr int HW = HT / 64;
 
+// Sequence b's logits and mask from its partial z: z[j] as 4 fixed quarters of the strips,
+// each summed in strip order, then the quarters in order; ReLU, W2, threshold.  The whole
+// workgroup (NT threads) calls it.
+template <int NT>
+__device__ void finish_seq(const float* __restrict__ zpart, int b, int nch, int d_router,
+                           const float* __restrict__ w2, int n_kv_heads, float threshold,
+                           float* __restrict__ logits, int32_t* __restrict__ mask,
+                           float (&zq)[4][ROUTE_MAX_DR], float (&zs)[ROUTE_MAX_DR]) {
+  const int tid = threadIdx.x;
+  {
+    const int q4 = tid & 3, per = (nch + 3) / 4;
+    for (int j = tid / 4; j < d_router; j += NT / 4) {
+      float z = 0.f;
+      const int c1 = min(nch, (q4 + 1) * per);
+      for (int cs0 = q4 * per; cs0 < c1; cs0 += 16) {
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          x[r] = cs0 + r < c1 ? zpart[((int64_t)b * nch + cs0 + r) * ROUTE_MAX_DR + j] : 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) z += x[r];
+      }
+      zq[q4][j] = z;
+    }
+  }
+  __syncthreads();
+  for (int j = tid; j < d_router; j += NT) zs[j] = fmaxf(((zq[0][j] + zq[1][j]) + zq[2][j]) + zq[3][j], 0.f);
+  __syncthreads();
+  for (int gh = tid; gh < n_kv_heads; gh += NT) {
+    const float* wg = w2 + (int64_t)gh * d_router;
+    float acc = 0.f;
+    for (int r = 0; r < d_router; ++r) acc = fmaf(wg[r], zs[r], acc);
+    if (logits) logits[(int64_t)b * n_kv_heads + gh] = acc;
+    mask[(int64_t)b * n_kv_heads + gh] = acc > threshold ? 1 : 0;
+  }
+}
+
 __global__ __launch_bounds__(HT) void route_strip(
     const float* __restrict__ partials, const int32_t* __restrict__ cu, int batch, int64_t total,
     int d, int pool_head, int pool_tail, int slab_rows, const float* __restrict__ w1, int d_router,
-    float* __restrict__ zpart) {
+    float* __restrict__ zpart, int32_t* __restrict__ done, const float* __restrict__ w2,
+    int n_kv_heads, float threshold, float* __restrict__ logits, int32_t* __restrict__ mask) {
   __shared__ float red[HW][HCOLS];
   __shared__ float hbar[HCOLS];
+  __shared__ float zq[4][ROUTE_MAX_DR];
+  __shared__ float zs[ROUTE_MAX_DR];
+  __shared__ int last;
   const int b = blockIdx.x, ch = blockIdx.y, nch = gridDim.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int first, seq;
@@ -343,45 +391,20 @@ __global__ __launch_bounds__(HT) void route_strip(
     acc += __shfl_xor(acc, 2);
     if (jrow < d_router && q4 == 0) zpart[((int64_t)b * nch + ch) * ROUTE_MAX_DR + jrow] = acc;
   }
-}
 
-constexpr int FT = 256;  // threads of route_finish
-
-__global__ __launch_bounds__(FT) void route_finish(const float* __restrict__ zpart, int nch,
-                                                   int d_router, const float* __restrict__ w2,
-                                                   int n_kv_heads, float threshold,
-                                                   float* __restrict__ logits,
-                                                   int32_t* __restrict__ mask) {
-  __shared__ float zq[4][ROUTE_MAX_DR];
-  __shared__ float zs[ROUTE_MAX_DR];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  // z[j]: 4 threads per row each sum a quarter of the strips in order, then the quarters
-  {
-    const int q4 = tid & 3, per = (nch + 3) / 4;
-    for (int j = tid / 4; j < d_router; j += FT / 4) {
-      float z = 0.f;
-      const int c1 = min(nch, (q4 + 1) * per);
-      for (int cs0 = q4 * per; cs0 < c1; cs0 += 16) {
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          x[r] = cs0 + r < c1 ? zpart[((int64_t)b * nch + cs0 + r) * ROUTE_MAX_DR + j] : 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) z += x[r];
-      }
-      zq[q4][j] = z;
-    }
+  // 3. the sequence's last workgroup finishes it.  The barrier orders every wave's partial z
+  //    before thread 0's device-scope release; the acquire after the count orders the other
+  //    workgroups' partial z before this workgroup's reads.
+  __syncthreads();
+  if (tid == 0) {
+    __threadfence();
+    const int prior = atomicAdd(done + b, 1);
+    if (prior == nch - 1) __threadfence();
+    last = prior == nch - 1;
   }
   __syncthreads();
-  for (int j = tid; j < d_router; j += FT) zs[j] = fmaxf(((zq[0][j] + zq[1][j]) + zq[2][j]) + zq[3][j], 0.f);
-  __syncthreads();
-  for (int gh = tid; gh < n_kv_heads; gh += FT) {
-    const float* wg = w2 + (int64_t)gh * d_router;
-    float acc = 0.f;
-    for (int r = 0; r < d_router; ++r) acc = fmaf(wg[r], zs[r], acc);
-    if (logits) logits[(int64_t)b * n_kv_heads + gh] = acc;
-    mask[(int64_t)b * n_kv_heads + gh] = acc > threshold ? 1 : 0;
-  }
+  if (!last) return;  // uniform
+  finish_seq<HT>(zpart, b, nch, d_router, w2, n_kv_heads, threshold, logits, mask, zq, zs);
 }
 
 }  // namespace
@@ -390,7 +413,7 @@ hipError_t launch_route(const void* hidden, int hidden_dtype, const int32_t* cu_
                         int64_t total_tokens, int d_model, int pool_head, int pool_tail,
                         const float* w1, int d_router, const float* w2, int n_kv_heads,
                         float threshold, float* logits_out, int32_t* mask_out, float* partials,
-                        int64_t max_slabs, float* zpart, hipStream_t stream) {
+                        int64_t max_slabs, float* zpart, int32_t* done, hipStream_t stream) {
   const int chunks = (d_model + RCOLS - 1) / RCOLS;
   // Boundary pooling reads at most pool_head + pool_tail rows per sequence: the grid covers
   // those slabs only.
@@ -408,24 +431,21 @@ hipError_t launch_route(const void* hidden, int hidden_dtype, const int32_t* cu_
   if ((int64_t)nslab * chunks <= 1024) {
     auto pool = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, dim3(nslab, chunks), dim3(512), 0, stream, hidden, cu_seqlens,
-                         batch, total_tokens, d_model, pool_head, pool_tail, slab_rows, partials);
+                         batch, total_tokens, d_model, pool_head, pool_tail, slab_rows, partials, done);
     };
     if (hidden_dtype == ELASTIC_BF16) pool(route_pool_partial_1r<ELASTIC_BF16>);
     else pool(route_pool_partial_1r<ELASTIC_FP32>);
   } else {
     hipLaunchKernelGGL(route_pool_partial, dim3(nslab, chunks), dim3(256), 0, stream, hidden,
                        hidden_dtype, cu_seqlens, batch, total_tokens, d_model, pool_head, pool_tail,
-                       slab_rows, partials);
+                       slab_rows, partials, done);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nch = (d_model + HCOLS - 1) / HCOLS;
   hipLaunchKernelGGL(route_strip, dim3(batch, nch), dim3(HT), 0, stream, partials, cu_seqlens, batch,
-                     total_tokens, d_model, pool_head, pool_tail, slab_rows, w1, d_router, zpart);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(route_finish, dim3(batch), dim3(FT), 0, stream, zpart, nch, d_router, w2,
-                     n_kv_heads, threshold, logits_out, mask_out);
+                     total_tokens, d_model, pool_head, pool_tail, slab_rows, w1, d_router, zpart,
+                     done, w2, n_kv_heads, threshold, logits_out, mask_out);
   return hipGetLastError();
 }
 
