@@ -222,8 +222,8 @@ def test_router_boundary_pooling_and_empty_sequence():
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_router_ragged_strips_wide_mlp(dtype):
     """d_model not a multiple of the 64-column strip (last strip partial), a router width of 200
-    (several passes of the finishing kernel), 12 KV heads, a varlen batch; repeated calls agree
-    bit for bit."""
+    (several passes of the finishing step), 12 KV heads, a varlen batch; repeated calls agree
+    bit for bit, also on a reused workspace that starts as 0xFF bytes."""
     lens = [777, 64, 1, 2050]
     T, d, dr, hkv = sum(lens), 1000, 200, 12
     hidden = syn.draw_bf16_bits(31, 3, (T, d))
@@ -241,6 +241,14 @@ def test_router_ragged_strips_wide_mlp(dtype):
     np.testing.assert_array_equal(mask.cpu().numpy()[outside], ref["mask"][outside])
     logits2, _ = ext.route(H.to_dev(hidden), H.to_dev(w1), H.to_dev(w2), cu_seqlens=cu)
     np.testing.assert_array_equal(lg, logits2.cpu().numpy())
+    # a workspace that starts as 0xFF bytes, used twice: the per-sequence completion counts
+    # inside it are cleared by each call itself
+    ws = torch.full((ext.route_workspace_size(len(lens), T, d),), 255, dtype=torch.uint8, device=H.DEV)
+    for _ in range(2):
+        logits3, mask3 = ext.route(H.to_dev(hidden), H.to_dev(w1), H.to_dev(w2), cu_seqlens=cu,
+                                   workspace=ws)
+        np.testing.assert_array_equal(lg, logits3.cpu().numpy())
+        np.testing.assert_array_equal(mask.cpu().numpy(), mask3.cpu().numpy())
 
 
 @pytest.mark.parametrize("frac", [0.0, 0.25, 0.5, 0.75, 1.0])
