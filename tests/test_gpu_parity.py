@@ -1,8 +1,9 @@
 """GPU parity of libelastic against the fp64 oracle, through the C ABI.
 
 Small cases compare every output element (several query and key tiles, ragged tails, GQA
-ratios 1/4/7/8, head dims 64/128, every sparse pattern, packed variable-length batches; the
-seeded sweep in test_gpu_sweep.py adds G = 2, 3, 5, 6, 16 and random patterns).
+ratios 1/4/7/8 and 32/64/128/256 (items of 8 query tokens down to one), head dims 64/128,
+every sparse pattern, packed variable-length batches; the seeded sweep in test_gpu_sweep.py
+adds G = 2, 3, 5, 6, 16 and random patterns).
 The five workload shapes are checked at full size in the launch configuration the
 benchmark times, on a deterministic row sample the oracle computes exactly: per sequence the
 first 2 * (sink + window) rows, every 16th block of 128 rows and the last block, for every
@@ -68,6 +69,14 @@ SMALL = [
     ("varlen-mixed", [1, 129, 64, 250, 0, 77], 8, 2, 128, {"kind": "streaming", "sink": 3, "window": 40},
      [[1, 0], [0, 1], [0, 0], [1, 1], [0, 1], [0, 0]]),
     ("stream-window-covers-all", [200], 4, 1, 128, {"kind": "streaming", "sink": 0, "window": 4096}, [[0]]),
+    # large GQA ratios: items of 8, 4, 2 and 1 query tokens (256 / G), a wave's 32 rows a
+    # fraction of one token's heads
+    ("full-g32-d128", [150], 64, 2, 128, None, None),
+    ("stream-g64-d64", [137], 64, 1, 64, {"kind": "streaming", "sink": 5, "window": 40}, [[0]]),
+    ("block64-g128-d128", [200], 128, 1, 128,
+     {"kind": "block", "block": 64, "sink_blocks": 1, "local_blocks": 1, "stride_blocks": 2}, [[0]]),
+    ("varlen-g256-d64", [97, 0, 60], 256, 1, 64, {"kind": "streaming", "sink": 3, "window": 20},
+     [[1], [0], [0]]),
 ]
 
 
