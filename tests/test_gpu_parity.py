@@ -92,15 +92,16 @@ def test_small_bf16_every_element(case):
     np.testing.assert_allclose(lse, rl, rtol=0, atol=H.BF16_LSE_ATOL)
 
 
-@pytest.mark.parametrize("D", [64, 128])
-def test_small_fp32_every_element(D):
+@pytest.mark.parametrize("D,hq,hkv", [(64, 8, 2), (128, 8, 2), (128, 64, 2), (64, 256, 1)])
+def test_small_fp32_every_element(D, hq, hkv):
+    """GQA 4, and 32 and 256 (items of 8 query tokens and of one)."""
     seqlens = [190, 67]
     sparse = {"kind": "block", "block": 64, "sink_blocks": 1, "local_blocks": 1, "stride_blocks": 2}
-    mask = [[1, 0], [0, 1]]
-    data = _bf16_case(11, seqlens, 8, 2, D, scale=1.0, dtype="f32")
+    mask = [[1, 0], [0, 1]] if hkv == 2 else [[1], [0]]
+    data = _bf16_case(11, seqlens, hq, hkv, D, scale=1.0, dtype="f32")
     o, lse = _run_attn(data, seqlens, mask, sparse)
     ro, rl = oracle.attention(data["q"], data["k"], data["v"], np.cumsum([0] + seqlens), mask, sparse)
-    H.assert_f32_close(o, ro, f"fp32 D={D}")
+    H.assert_f32_close(o, ro, f"fp32 D={D} G={hq // hkv}")
     np.testing.assert_allclose(lse, rl, rtol=0, atol=1e-5)
 
 
