@@ -13,9 +13,10 @@
 // retrieval_combine: one workgroup per (sequence, KV head) merges the chunks of each query
 //   head (lanes over chunks, a fixed butterfly across lanes), S = ln / l, and averages the G
 //   query heads in head order for the KV head.
-// assign_kernel: one workgroup ranks the N units (scores, staged in LDS) by counting: unit i is full when
-//   fewer than k units rank above it (higher score; equal score and lower index; NaN below
-//   every number).
+// assign_kernel: ranks the N units (scores, staged in LDS by every workgroup) by counting, one
+//   wave per unit: unit i is full when fewer than k units rank above it (higher score; equal
+//   score and lower index; NaN below every number).
+#include <algorithm>
 #include <type_traits>
 
 #include "elastic_internal.hpp"
@@ -187,34 +188,33 @@ __global__ __launch_bounds__(RET_THREADS) void retrieval_combine(
   }
 }
 
-// one workgroup; unit i is full iff fewer than k units rank above it.  T = 1024 / n lanes (a
-// power of two, at most 64) share the comparisons of one unit and add their counts.
-__global__ __launch_bounds__(1024) void assign_kernel(const float* __restrict__ scores, int n,
-                                                      int k, int32_t* __restrict__ mask) {
+// Unit i is full iff fewer than k units rank above it.  Every workgroup stages all n scores
+// in LDS; each wave ranks one unit at a time (the grid's waves stride over the units), its 64
+// lanes splitting the n comparisons, and adds the counts across the wave.  (One workgroup
+// doing all n^2 comparisons took 12.9 us for 256 units, bound by one CU's VALU.)
+constexpr int ASSIGN_THREADS = 256;
+__global__ __launch_bounds__(ASSIGN_THREADS) void assign_kernel(const float* __restrict__ scores,
+                                                                int n, int k,
+                                                                int32_t* __restrict__ mask) {
   __shared__ float s_sc[ELASTIC_ASSIGN_MAX_UNITS];
-  for (int i = threadIdx.x; i < n; i += 1024) s_sc[i] = scores[i];
+  for (int i = threadIdx.x; i < n; i += ASSIGN_THREADS) s_sc[i] = scores[i];
   __syncthreads();
-  int T = 1;
-  while (T < 64 && T * 2 * n <= 1024) T *= 2;
-  const int per_pass = 1024 / T;
-  const int t = threadIdx.x & (T - 1);
-  for (int base = 0; base < n; base += per_pass) {  // uniform trip count
-    const int i = base + (int)threadIdx.x / T;
+  const int lane = threadIdx.x & 63;
+  const int waves = (int)gridDim.x * (ASSIGN_THREADS / 64);
+  for (int i = (int)blockIdx.x * (ASSIGN_THREADS / 64) + (int)(threadIdx.x >> 6); i < n; i += waves) {
+    const float si = s_sc[i];
+    const bool ni = si != si;
     int above = 0;
-    if (i < n) {
-      const float si = s_sc[i];
-      const bool ni = si != si;
-      for (int j = t; j < n; j += T) {
-        const float sj = s_sc[j];
-        const bool nj = sj != sj;
-        // j ranks above i: a number above NaN; higher score; equal score and lower index
-        const bool up = (!nj && ni) || (!nj && !ni && (sj > si || (sj == si && j < i))) ||
-                        (nj && ni && j < i);
-        above += up ? 1 : 0;
-      }
+    for (int j = lane; j < n; j += 64) {
+      const float sj = s_sc[j];
+      const bool nj = sj != sj;
+      // j ranks above i: a number above NaN; higher score; equal score and lower index
+      const bool up = (!nj && ni) || (!nj && !ni && (sj > si || (sj == si && j < i))) ||
+                      (nj && ni && j < i);
+      above += up ? 1 : 0;
     }
-    for (int off = T / 2; off >= 1; off >>= 1) above += __shfl_xor(above, off, 64);
-    if (i < n && t == 0) mask[i] = above < k ? 1 : 0;
+    for (int off = 32; off >= 1; off >>= 1) above += __shfl_xor(above, off, 64);
+    if (lane == 0) mask[i] = above < k ? 1 : 0;
   }
 }
 
@@ -265,7 +265,10 @@ hipError_t launch_retrieval(int dtype, int head_dim, const void* q, const void* 
 }
 
 hipError_t launch_assign(const float* scores, int n, int k, int32_t* mask, hipStream_t stream) {
-  hipLaunchKernelGGL(assign_kernel, dim3(1), dim3(1024), 0, stream, scores, n, k, mask);
+  const int units_per_wg = ASSIGN_THREADS / 64;
+  const int grid = std::min((n + units_per_wg - 1) / units_per_wg, 1024);
+  hipLaunchKernelGGL(assign_kernel, dim3((unsigned)std::max(grid, 1)), dim3(ASSIGN_THREADS), 0, stream,
+                     scores, n, k, mask);
   return hipGetLastError();
 }
 

@@ -263,7 +263,8 @@ int elastic_retrieval_scores(const void* q, const void* k, int32_t dtype,
  *   k = floor((1 - omega_msr) * n_units)       (evaluated in double)
  * highest stay full: mask_out[i] = 1, the rest 0 (device int32 [n_units]).  Equal scores rank
  * by lower index; NaN ranks below every number.  A layer's slice of mask_out is a forced head
- * mask for elastic_attn_prefill.  One workgroup, O(n_units^2) comparisons.
+ * mask for elastic_attn_prefill.  One kernel, O(n_units^2) comparisons spread over up to 4096
+ * waves.
  * Errors: ELASTIC_EINVAL (pointers, omega_msr outside [0, 1]), ELASTIC_EUNSUPPORTED
  * (n_units > ELASTIC_ASSIGN_MAX_UNITS).
  */

@@ -78,7 +78,8 @@ def test_scores_32k_layer():
         np.testing.assert_allclose(H.to_f64(skv), rkv, rtol=0, atol=1e-4)
 
 
-@pytest.mark.parametrize("shape,seed", [((32, 8), 0), ((1, 1), 1), ((4, 7), 2), ((128, 32), 3)])
+@pytest.mark.parametrize("shape,seed", [((32, 8), 0), ((1, 1), 1), ((4, 7), 2), ((128, 32), 3),
+                                        ((128, 128), 4)])
 def test_assignment_bit_exact(shape, seed):
     rng = np.random.default_rng(seed)
     s = np.round(rng.random(shape), 2).astype(np.float32)   # many ties
