@@ -238,6 +238,9 @@ def _time_attn(ext, torch, stream, fn, reps=10, warm=3, min_warm_ms=50.0):
             torch.cuda.synchronize()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # about 1 ms of GPU work ahead of the events: the calls queue up behind it, so a call of a
+    # few microseconds is timed on the GPU, not at the host's launch rate
+    torch.cuda._sleep(2_000_000)
     a.record(stream)
     for _ in range(reps):
         fn()
