@@ -123,7 +123,9 @@ size_t elastic_route_workspace_size(int32_t batch, int64_t total_tokens, int32_t
  *  mask_out    [batch, n_kv_heads] int32, 1 = full attention, 0 = sparse (required)
  *  d_model     multiple of 8.  Sums are fp32 in a fixed order: results are bitwise
  *              reproducible run to run.  A sequence of length 0 pools nothing: its
- *              logits are 0 and its mask is all sparse.
+ *              logits are 0, so its mask is (0 > threshold): all sparse for threshold >= 0.
+ * The workspace holds intermediate sums and per-sequence completion counts that the call
+ * itself clears; two calls in flight at once need two workspaces.
  */
 int elastic_route(const void* hidden, int32_t hidden_dtype, const int32_t* cu_seqlens,
                   int32_t batch, int64_t total_tokens, int32_t d_model, int32_t pool_head,
