@@ -439,7 +439,7 @@ def streaming_scaling(ext, torch, stream):
 
 def _host_cpu():
     """(threads the oracle uses, CPUs visible to this process, CPU model).  The oracle's pool is
-    capped at 16 threads: the GPU machine's CPU share for one GPU."""
+    capped at 16 threads, a one-GPU share of a multi-GPU host's cores."""
     try:
         visible = len(os.sched_getaffinity(0))
     except AttributeError:
