@@ -41,6 +41,9 @@ CASES = [
     ("block-g4-d64", [517], 8, 2, 64, BLOCK, [[0, 1]]),
     ("bstream-g7-d128", [450], 14, 2, 128, BSTREAM, [[0, 1]]),
     ("full-g8-d128", [333], 8, 1, 128, None, None),
+    # large GQA ratios: items of 8 and of one query token
+    ("stream-g32-d128", [300], 64, 2, 128, STREAM, [[0, 1]]),
+    ("block-g256-d64", [150], 256, 1, 64, BLOCK, [[0]]),
 ]
 
 
