@@ -62,6 +62,8 @@ CASES = [
     ("g4-d128-b128", [700], 4, 1, 128, 128, "bf16", [[0]]),
     ("varlen", [130, 1, 300, 64], 8, 2, 128, 64, "bf16", [[0, 1], [0, 0], [1, 0], [0, 0]]),
     ("fp32-d64", [333], 8, 2, 64, 64, "f32", [[0, 0]]),
+    ("g32-d128-b64", [300], 64, 2, 128, 64, "bf16", [[0, 0]]),   # items of 8 query tokens
+    ("g256-d64-b128", [200], 256, 1, 64, 128, "bf16", [[0]]),    # items of one query token
 ]
 
 
