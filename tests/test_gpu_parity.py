@@ -105,6 +105,32 @@ def test_small_fp32_every_element(D, hq, hkv):
     np.testing.assert_allclose(lse, rl, rtol=0, atol=1e-5)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("scale", [0.02, 0.3])
+def test_explicit_softmax_scale(dtype, scale):
+    """A softmax scale other than 1/sqrt(D): a flat one (0.02) and a sharp one (0.3, scores
+    several times larger, so the running maximum is raised often)."""
+    seqlens = [260, 0, 97]
+    sparse = {"kind": "streaming", "sink": 8, "window": 64}
+    mask = [[1, 0], [0, 1], [1, 1]]
+    data = _bf16_case(13, seqlens, 8, 2, 128, scale=1.0, dtype=dtype)
+    q, k, v = H.to_dev(data["q"]), H.to_dev(data["k"]), H.to_dev(data["v"])
+    T = sum(seqlens)
+    cu_np = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int32)
+    l = torch.full((8, T), float("nan"), dtype=torch.float32, device=H.DEV)
+    o = ext.attn_prefill(q, k, v, cu_seqlens=torch.tensor(cu_np, device=H.DEV), max_seqlen=max(seqlens),
+                         head_mask=torch.tensor(mask, dtype=torch.int32, device=H.DEV), sparse=sparse,
+                         softmax_scale=scale, lse=l)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(data["q"], data["k"], data["v"], cu_np, mask, sparse, scale=scale)
+    if dtype == "bf16":
+        H.assert_bf16_close(H.to_f64(o), ro, f"scale {scale}")
+        np.testing.assert_allclose(H.to_f64(l), rl, rtol=0, atol=H.BF16_LSE_ATOL)
+    else:
+        H.assert_f32_close(H.to_f64(o), ro, f"scale {scale}")
+        np.testing.assert_allclose(H.to_f64(l), rl, rtol=0, atol=1e-5)
+
+
 def test_fp32_512_workload_full_size():
     w = syn.WORKLOADS["fp32-512-s4w64"]
     data = syn.make_qkv(w)
